@@ -1,0 +1,458 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each check is a function of the implementation under test, so the mutation
+tests at the bottom can show that a plausible mistake planted in a copy of
+the oracle fails at least one pin.
+"""
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------ independent helpers
+def half_of_fraction(x: Fraction) -> float:
+    """IEEE binary16 round-half-even of an exact rational (independent of numpy)."""
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    ax = abs(x)
+    e = 0
+    while ax >= Fraction(2) ** (e + 1):
+        e += 1
+    while ax < Fraction(2) ** e:
+        e -= 1
+    e = max(e, -14)                     # subnormals share the 2**-24 quantum
+    quantum = Fraction(2) ** (e - 10)
+    n = round(ax / quantum)             # Fraction.__round__ is half-to-even
+    v = n * quantum
+    if v > 65504:
+        return sign * float("inf")
+    return sign * float(v)
+
+
+def half_bits_struct(x: float) -> int:
+    """binary16 bits of a float via Python's struct (round-half-even)."""
+    return struct.unpack("<H", struct.pack("<e", x))[0]
+
+
+def read_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            rows.append(line)
+    return rows
+
+
+# ------------------------------------------------------------ rational rounding
+def test_rne_ratio_matches_fraction_round():
+    nums = np.arange(-300, 301)
+    for den in range(1, 21):
+        got = ref.rne_ratio(nums, den)
+        want = [round(Fraction(int(n), den)) for n in nums]
+        assert got.tolist() == want
+
+
+def test_ceil_ratio():
+    for num in range(-50, 260):
+        for den in (1, 2, 7, 15):
+            assert ref.ceil_ratio(num, den) == -((-num) // den)
+            assert ref.ceil_ratio(num, den) == int(np.ceil(Fraction(num, den)))
+
+
+# ------------------------------------------------------------ fp16 conversions
+def test_to_f16_matches_exact_rational_rounding():
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([
+        rng.standard_normal(3000).astype(np.float32) * np.float32(10.0) ** rng.integers(-8, 5, 3000),
+        np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -25, 3 * 2 ** -25, 65519.0, 65520.0,
+                  2 ** -14 * (1 - 2 ** -11)], dtype=np.float32)])
+    got = ref.to_f16(vals.astype(np.float32)).astype(np.float64)
+    for v, g in zip(vals, got):
+        want = half_of_fraction(Fraction(float(v)))
+        assert g == want or (np.isinf(g) and np.isinf(want)), (v, g, want)
+
+
+# ------------------------------------------------------------ O2 level 2
+def level2_domain_check(level2, limit=119):
+    """Exhaustive over every (lo, hi, w8) with -limit <= lo <= 0 <= hi <= limit.
+
+    A level-2 result for one element depends only on its group's lo, hi and
+    on its own value, so groups [lo, hi, lo..hi] cover the whole domain.
+    Returns the number of violations of: s2 in [1,16], z in [0,15],
+    q in [0,15], decode in int8, and |w8 - decode| <= s2/2 (where unclamped).
+    """
+    width = 2 * limit + 3
+    los, his = np.meshgrid(np.arange(-limit, 1), np.arange(0, limit + 1), indexing="ij")
+    los = los.ravel()
+    his = his.ravel()
+    offs = np.arange(width - 2)
+    vals = los[:, None] + offs[None, :]
+    vals = np.minimum(vals, his[:, None])           # pad with hi (inside the group)
+    groups = np.concatenate([los[:, None], his[:, None], vals], axis=1)
+    s2, z, q = level2(groups)
+    s2 = s2.astype(np.int64)
+    z = z.astype(np.int64)
+    q = q.astype(np.int64)
+    dec = (q - z[:, None]) * s2[:, None]
+    bad = 0
+    bad += int(np.sum((s2 < 1) | (s2 > 16)))
+    bad += int(np.sum((z < 0) | (z > 15)))
+    bad += int(np.sum((q < 0) | (q > 15)))
+    bad += int(np.sum((dec < -128) | (dec > 127)))
+    err = np.abs(groups - dec)
+    # a clamp to 15 can add one extra step; otherwise the error is <= s2/2
+    unclamped = q < 15
+    bad += int(np.sum((2 * err > s2[:, None]) & unclamped))
+    bad += int(np.sum(err > s2[:, None] + s2[:, None] // 2))
+    return bad
+
+
+def test_level2_exhaustive_domain():
+    assert level2_domain_check(ref.level2_groups) == 0
+
+
+def test_level1_range_119_is_the_widest_safe_range():
+    # The +-119 reading: every decode stays in int8 at 119, not at 120.
+    assert level2_domain_check(ref.level2_groups, limit=119) == 0
+    assert level2_domain_check(ref.level2_groups, limit=120) > 0
+
+
+def level2_golden_check(level2):
+    bad = []
+    for line in read_rows("level2_cases.txt"):
+        lo, hi, w8, s2_w, z_w, q_w, dec_w = (int(t) for t in line.split())
+        group = np.array([[lo, hi, w8]])
+        s2, z, q = level2(group)
+        dec = (int(q[0, 2]) - int(z[0])) * int(s2[0])
+        if (int(s2[0]), int(z[0]), int(q[0, 2]), dec) != (s2_w, z_w, q_w, dec_w):
+            bad.append((line, int(s2[0]), int(z[0]), int(q[0, 2]), dec))
+    return bad
+
+
+def test_level2_golden():
+    assert level2_golden_check(ref.level2_groups) == []
+
+
+def test_level2_identity_special_case():
+    # W8 in [0, 15] -> s2 = 1, z = 0, q = W8: decode is the identity.
+    rng = np.random.default_rng(0)
+    g = rng.integers(0, 16, size=(100, 128))
+    g[:, 0] = 15
+    s2, z, q = ref.level2_groups(g)
+    assert (s2 == 1).all() and (z == 0).all() and (q == g).all()
+
+
+# ------------------------------------------------------------ O1 level 1
+def test_level1_golden():
+    for line in read_rows("level1_cases.txt"):
+        body = line.split(":", 1)[1]
+        vals, s1_w, w8_w = (p.split() for p in body.split("|"))
+        w = np.array([[float(v) for v in vals]], dtype=np.float32)
+        s1, w8 = ref.level1_rows(w)
+        assert float(s1[0]) == float(s1_w[0]), line
+        assert w8[0].tolist() == [int(t) for t in w8_w], line
+
+
+def level1_invariant_check(level1, w):
+    """Closed-form invariants of level 1 on rows with a normal fp16 scale."""
+    s1, w8 = level1(w)
+    s = s1.astype(np.float64)
+    alpha = np.abs(w).max(axis=1).astype(np.float64)
+    problems = 0
+    # scale is fp16(fp32(alpha / 119)), checked through an independent rounding
+    for i in range(0, w.shape[0], max(1, w.shape[0] // 64)):
+        want = half_of_fraction(Fraction(float(np.float32(alpha[i]) / np.float32(119))))
+        problems += float(s1[i]) != want
+    problems += int(np.sum(np.abs(w8) > 119))
+    # absmax element maps to exactly +-119 (fp16 scale off by <= 2**-11 relative)
+    arg = np.abs(w).argmax(axis=1)
+    top = w8[np.arange(w.shape[0]), arg]
+    problems += int(np.sum(np.abs(top) != 119))
+    # sign agrees, and reconstruction error <= s1/2 (+ fp32 product rounding)
+    recon = s[:, None] * w8
+    problems += int(np.sum(np.abs(w - recon) > s[:, None] * (0.5 + 2 ** -10)))
+    problems += int(np.sum(np.sign(w8) * np.sign(w) < 0))
+    return problems
+
+
+def test_level1_invariants_random_rows():
+    w = synth.weights(512, 256, seed=11)
+    assert level1_invariant_check(ref.level1_rows, w) == 0
+    w = synth.weights(256, 512, seed=12, dist="student_t4")
+    assert level1_invariant_check(ref.level1_rows, w) == 0
+
+
+def test_level1_zero_row_and_tiny_scale():
+    w = np.zeros((3, 64), dtype=np.float32)
+    w[1, 3] = 1e-4                      # 1e-4/119: subnormal fp16 scale
+    w[2, 5] = 1e-7                      # 1e-7/119 underflows: scale 0, row 0
+    s1, w8 = ref.level1_rows(w)
+    assert float(s1[0]) == 0 and not w8[0].any()
+    assert 0 < float(s1[1]) < 2 ** -14 and abs(w8[1]).max() <= 119
+    assert float(s1[2]) == 0 and not w8[2].any()
+
+
+# ------------------------------------------------------------ O1' per channel
+def test_per_channel_invariants():
+    w = synth.weights(300, 256, seed=13, dist="student_t4")
+    s1, q, z, s2 = ref.per_channel(w)
+    assert (s2 == 1).all() and q.max() <= 15 and z.max() <= 15
+    s = s1.astype(np.float64)
+    dec = q.astype(np.int64) - z.astype(np.int64)
+    err = np.abs(w - s[:, None] * dec)
+    # unclamped elements: error <= s1/2 (+ fp32 rounding); clamped ones <= 1.5 s1
+    assert (err <= s[:, None] * (1.5 + 2 ** -10)).all()
+    assert np.mean(err <= s[:, None] * (0.5 + 2 ** -10)) > 0.99
+    # zero representable: a zero weight decodes to exactly 0
+    w2 = w.copy()
+    w2[:, 7] = 0
+    s1b, qb, zb, _ = ref.per_channel(w2)
+    assert (qb[:, 7].astype(int) == zb[:, 0].astype(int)).all()
+
+
+def test_per_channel_hand_case():
+    # lo = -1.5, hi = 6: (6 + 1.5)/15 = 0.5 -> s1 = 0.5, r = 2, z = rint(3) = 3
+    w = np.array([[-1.5, 6.0, 0.25, 0.75, -0.25, 0.0, 1.0, 2.0]], dtype=np.float32)
+    s1, q, z, s2 = ref.per_channel(w)
+    assert float(s1[0]) == 0.5 and int(z[0, 0]) == 3
+    # q = rint(2w) + 3: -3+3, 12+3, rint(0.5)=0 -> 3, rint(1.5)=2 -> 5, rint(-0.5)=0 -> 3, 3, 5, 7
+    assert q[0].tolist() == [0, 15, 3, 5, 3, 3, 5, 7]
+
+
+# ------------------------------------------------------------ O3 activations
+def test_act_golden():
+    for line in read_rows("act_cases.txt"):
+        body = line.split(":", 1)[1]
+        vals, s_w, a8_w = (p.split() for p in body.split("|"))
+        a = np.array([[float(v) for v in vals]], dtype=np.float16)
+        a8, s_a = ref.quant_act(a)
+        assert float(s_a[0]) == float(s_w[0]), line
+        assert a8[0].tolist() == [int(t) for t in a8_w], line
+
+
+def act_scale_sweep_check(quant_act):
+    """Every positive finite fp16 absmax value, one token each."""
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    alpha = bits.view(np.float16)
+    m = alpha.size
+    a = np.zeros((m, 8), dtype=np.float16)
+    a[:, 0] = alpha
+    a[:, 1] = -(alpha / np.float16(3))
+    a[:, 2] = alpha * np.float16(0.5)
+    a8, s_a = quant_act(a)
+    problems = 0
+    # independent scale: fp16 of the fp32 quotient, through struct
+    q32 = alpha.astype(np.float32) / np.float32(127)
+    want_bits = np.array([half_bits_struct(float(v)) for v in q32], dtype=np.uint16)
+    problems += int(np.sum(s_a.view(np.uint16) != want_bits))
+    problems += int(np.sum(np.abs(a8.astype(int)) > 127))
+    normal = s_a.astype(np.float32) >= np.float32(2 ** -14)
+    problems += int(np.sum(a8[normal, 0] != 127))
+    # symmetry: quantizing -A gives -A8
+    a8n, _ = quant_act(-a)
+    problems += int(np.sum(a8n.astype(int) != -a8.astype(int)))
+    return problems
+
+
+def test_act_exhaustive_fp16_scale_sweep():
+    assert act_scale_sweep_check(ref.quant_act) == 0
+
+
+def test_act_reconstruction_bound():
+    a = synth.activations(64, 512, seed=3)
+    a8, s_a = ref.quant_act(a)
+    s = s_a.astype(np.float64)
+    err = np.abs(a.astype(np.float64) - s[:, None] * a8)
+    assert (err <= s[:, None] * (0.5 + 2 ** -10)).all()
+
+
+# ------------------------------------------------------------ O4 GEMM
+def brute_acc(a8, w8hat):
+    m, k = a8.shape
+    n = w8hat.shape[0]
+    out = np.zeros((m, n), dtype=np.int64)
+    for i in range(m):
+        for j in range(n):
+            s = 0
+            for t in range(k):
+                s += int(a8[i, t]) * int(w8hat[j, t])
+            out[i, j] = s
+    return out
+
+
+def gemm_brute_check(gemm):
+    rng = np.random.default_rng(7)
+    a8 = rng.integers(-127, 128, size=(3, 67)).astype(np.int8)
+    w8 = rng.integers(-128, 128, size=(5, 67)).astype(np.int32)
+    return np.array_equal(gemm(a8, w8), brute_acc(a8, w8))
+
+
+def test_gemm_brute_force():
+    assert gemm_brute_check(ref.gemm_acc)
+
+
+def test_gemm_extremes_exact():
+    k = 24576                                   # deepest layer of the workloads
+    a8 = np.full((2, k), 127, dtype=np.int8)
+    a8[1] = -127
+    w8 = np.full((3, k), -128, dtype=np.int32)
+    w8[1] = 127
+    acc = ref.gemm_acc(a8, w8)
+    assert acc[0, 0] == 127 * -128 * k and acc[1, 1] == -127 * 127 * k
+
+
+def test_dequant_then_matmul_matches_scaled_acc():
+    # float dequant-then-matmul equals s_a * s1 * acc up to fp64 rounding
+    w = synth.weights(48, 256, seed=21)
+    a = synth.activations(5, 256, seed=22)
+    out = ref.linear(a, w, 64)
+    wd = out["qw"]["s1"].astype(np.float64)[:, None] * out["w8hat"]
+    ad = out["s_a"].astype(np.float64)[:, None] * out["a8"].astype(np.float64)
+    y_float = ad @ wd.T
+    y_int = (out["acc"] * out["s_a"].astype(np.float64)[:, None]
+             * out["qw"]["s1"].astype(np.float64)[None, :])
+    assert np.allclose(y_float, y_int, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ O5 epilogue
+def test_epilogue_single_rounding():
+    rng = np.random.default_rng(9)
+    acc = rng.integers(-3 * 10 ** 8, 3 * 10 ** 8, size=(20, 30))
+    s_a = (rng.random(20) * 0.05 + 1e-4).astype(np.float16)
+    s1 = (rng.random(30) * 0.001 + 1e-5).astype(np.float16)
+    y = ref.epilogue(acc, s_a, s1)
+    for i in range(0, 20, 3):
+        for j in range(0, 30, 4):
+            exact = Fraction(int(acc[i, j])) * Fraction(float(s_a[i])) * Fraction(float(s1[j]))
+            assert float(y[i, j]) == half_of_fraction(exact)
+
+
+def test_tolerance_rule():
+    y_ref = np.array([1.0, 100.0, 0.0, -3.0], dtype=np.float16)
+    assert ref.y_tolerance_ok(y_ref, y_ref).all()
+    one_ulp = np.nextafter(y_ref, np.float16(np.inf))
+    assert ref.y_tolerance_ok(one_ulp, y_ref).all()
+    far = y_ref + np.float16(1.0)
+    assert not ref.y_tolerance_ok(far, y_ref)[[0, 2, 3]].any()
+
+
+def test_whole_layer_smoke_bound():
+    # model accuracy is not pinned (needs trained weights); keep a loose bound
+    w = synth.weights(256, 512, seed=1)
+    a = synth.activations(16, 512, seed=2)
+    out = ref.linear(a, w, 128)
+    y_fp = a.astype(np.float64) @ w.astype(np.float64).T
+    rel = np.linalg.norm(out["y"].astype(np.float64) - y_fp) / np.linalg.norm(y_fp)
+    assert rel < 0.15
+
+
+# ------------------------------------------------------------ mutation tests
+def _mut_round_not_ceil(w8):
+    w8 = np.asarray(w8, dtype=np.int64)
+    lo = np.minimum(0, w8.min(axis=-1))
+    hi = np.maximum(0, w8.max(axis=-1))
+    s2 = np.maximum(1, ref.rne_ratio(hi - lo, 15))
+    z = ref.rne_ratio(-lo, s2)
+    q = ref.rne_ratio(w8, s2[..., None]) + z[..., None]
+    return s2, z, np.clip(q, 0, 15)
+
+
+def _mut_no_zero_in_range(w8):
+    w8 = np.asarray(w8, dtype=np.int64)
+    lo = w8.min(axis=-1)
+    hi = w8.max(axis=-1)
+    s2 = np.maximum(1, ref.ceil_ratio(hi - lo, 15))
+    z = ref.rne_ratio(-lo, s2)
+    q = ref.rne_ratio(w8, s2[..., None]) + z[..., None]
+    return s2, z, np.clip(q, 0, 15)
+
+
+def _mut_zero_sign(w8):
+    s2, z, q = ref.level2_groups(w8)
+    q2 = ref.rne_ratio(np.asarray(w8, np.int64), s2[..., None].astype(np.int64)) - z[..., None]
+    return s2, z, np.clip(q2, 0, 15)
+
+
+def _mut_floor_div(w8):
+    w8 = np.asarray(w8, dtype=np.int64)
+    lo = np.minimum(0, w8.min(axis=-1))
+    hi = np.maximum(0, w8.max(axis=-1))
+    s2 = np.maximum(1, ref.ceil_ratio(hi - lo, 15))
+    z = ref.rne_ratio(-lo, s2)
+    q = w8 // s2[..., None] + z[..., None]
+    return s2, z, np.clip(q, 0, 15)
+
+
+@pytest.mark.parametrize("mutant", [_mut_round_not_ceil, _mut_no_zero_in_range,
+                                    _mut_zero_sign, _mut_floor_div])
+def test_level2_pins_catch_mutants(mutant):
+    caught = level2_domain_check(mutant) > 0 or level2_golden_check(mutant) != []
+    assert caught
+
+
+def test_level1_pins_catch_mutants():
+    w = synth.weights(128, 256, seed=31)
+
+    def wrong_limit(x):                       # 127 instead of 119
+        x = np.asarray(x, np.float32)
+        s1 = ref.to_f16(np.abs(x).max(axis=1) / np.float32(127))
+        r = np.float32(1) / s1.astype(np.float32)
+        return s1, np.clip(np.rint(x * r[:, None]), -127, 127).astype(np.int32)
+
+    def truncating(x):                        # trunc instead of rint
+        s1, _ = ref.level1_rows(x)
+        r = np.float32(1) / s1.astype(np.float32)
+        return s1, np.clip(np.trunc(np.asarray(x, np.float32) * r[:, None]), -119, 119).astype(np.int32)
+
+    def f32_scale(x):                         # scale left in fp32, not fp16
+        x = np.asarray(x, np.float32)
+        s = np.abs(x).max(axis=1) / np.float32(119)
+        r = np.float32(1) / s
+        return s, np.clip(np.rint(x * r[:, None]), -119, 119).astype(np.int32)
+
+    for mutant in (wrong_limit, truncating, f32_scale):
+        assert level1_invariant_check(mutant, w) > 0, mutant.__name__
+
+
+def test_act_pins_catch_mutants():
+    def floor_round(a):
+        a32 = np.asarray(a, np.float16).astype(np.float32)
+        s_a = ref.to_f16(np.abs(a32).max(axis=1) / np.float32(127))
+        r = np.zeros_like(s_a, dtype=np.float32)
+        nz = s_a != 0
+        r[nz] = np.float32(1) / s_a[nz].astype(np.float32)
+        return np.clip(np.floor(a32 * r[:, None] + 0.5), -127, 127).astype(np.int8), s_a
+
+    def divide_by_128(a):
+        a32 = np.asarray(a, np.float16).astype(np.float32)
+        s_a = ref.to_f16(np.abs(a32).max(axis=1) / np.float32(128))
+        r = np.zeros_like(s_a, dtype=np.float32)
+        nz = s_a != 0
+        r[nz] = np.float32(1) / s_a[nz].astype(np.float32)
+        return np.clip(np.rint(a32 * r[:, None]), -127, 127).astype(np.int8), s_a
+
+    assert act_scale_sweep_check(floor_round) > 0
+    assert act_scale_sweep_check(divide_by_128) > 0
+
+
+def test_gemm_pins_catch_mutants():
+    def transposed_k(a8, w8):                 # reversed k order on one operand
+        return ref.gemm_acc(a8, w8[:, ::-1])
+
+    def int16_wrap(a8, w8):                   # accumulator wrapped to int16
+        s = ref.gemm_acc(a8, w8)
+        return (s + 2 ** 15) % 2 ** 16 - 2 ** 15
+
+    assert not gemm_brute_check(transposed_k)
+    assert not gemm_brute_check(int16_wrap)
