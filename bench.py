@@ -1,0 +1,273 @@
+"""Benchmark of the W4A8 linear layer on one MI355X.
+
+One step = one pass of the whole hot path over a workload: for every run
+(M, layer) of the workload, the per-token activation quantizer followed by
+the W4A8 GEMM, each through the C ABI library.  Inputs are resident in HBM
+when the timed region starts.  Weight blobs rotate through a pool of copies
+of at least 1 GiB so that every GEMM reads its weights from HBM rather than
+from the 256 MB Infinity Cache or the L2.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
+GEMM_SRC = os.path.join(ROOT, "w4a8_gemm_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+
+
+def algo_bytes(m, n, k, g):
+    """Bytes the method must move: codes, group meta, s1, A8, s_a, Y."""
+    meta = 0.5 * n if g in (0, k) else 1.5 * n * k / g
+    return n * k / 2 + meta + 2 * n + m * k + 2 * m + 2 * m * n
+
+
+def quant_bytes(m, k):
+    return 3 * m * k + 2 * m
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(runs, weights, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample of the same workload: every
+    run, restricted to the first `cols` output columns of each layer."""
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    cols = 512
+    qws = {}
+    for (layer, n, k, g), w in weights.items():
+        qws[layer] = ref.quantize_weights(w[:cols], g)      # offline pack: not timed
+    acts = {}
+    for (m, layer, n, k, g, seed) in runs:
+        acts[(m, layer)] = synth.activations(m, k, seed=seed)
+    done_bytes = 0.0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for (m, layer, n, k, g, seed) in runs:
+            a = acts[(m, layer)]
+            a8, s_a = ref.quant_act(a)
+            w8hat = ref.decoded_weights(qws[layer])
+            acc = ref.gemm_acc(a8, w8hat)
+            ref.epilogue(acc, s_a, qws[layer]["s1"])
+            done_bytes += algo_bytes(m, cols, k, g) + quant_bytes(m, k)
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s or passes >= 50:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"every run of the workload restricted to the first {cols} output "
+                      f"columns of each layer, {passes} pass(es), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_decode",
+                    choices=[k for k in synth.workloads() if k != "tiny"] + ["tiny"])
+    ap.add_argument("--rotation-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--runs-json", default="")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this W4A8 GEMM build has no multi-GPU path "
+              "(the layer would shard by output columns or by K with an int32 all-reduce; "
+              "neither is built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w4a8_gemm_amd as w4
+    dev = torch.device("cuda:0")
+
+    wl_names = list(synth.workloads().keys())
+    items = synth.workloads()[args.workload]
+    cfg_idx = wl_names.index(args.workload)
+
+    # weights: one per (layer, g); seeds as the parity tests use them
+    layer_keys = []
+    for (_, m, layer, n, k, g, dist) in items:
+        key = (layer, n, k, g, dist)
+        if key not in layer_keys:
+            layer_keys.append(key)
+    weights, blobs = {}, {}
+    for shape_idx, (layer, n, k, g, dist) in enumerate(layer_keys):
+        log(f"packing {layer} n={n} k={k} g={g}")
+        w = synth.weights(n, k, seed=synth.weight_seed(cfg_idx, shape_idx, 0), dist=dist)
+        blobs[(layer, g)] = w4.to_device(w4.pack(w, g), dev)
+        if not args.no_cpu_baseline:
+            weights[(layer, n, k, g)] = w[:512].copy()
+        del w
+    per_copy = sum(b.numel() for b in blobs.values())
+    ncopies = max(2, int(np.ceil(args.rotation_gib * 2 ** 30 / per_copy)))
+    pool = [blobs] + [{key: b.clone() for key, b in blobs.items()} for _ in range(ncopies - 1)]
+    log(f"rotation pool: {ncopies} copies x {per_copy / 2**20:.1f} MiB")
+
+    runs = []   # (m, layer, n, k, g, seed)
+    m_index = {}
+    for (_, m, layer, n, k, g, dist) in items:
+        shape_idx = layer_keys.index((layer, n, k, g, dist))
+        mi = m_index.setdefault((layer, g), {}).setdefault(m, len(m_index[(layer, g)]))
+        runs.append((m, layer, n, k, g, synth.act_seed(cfg_idx, shape_idx, mi)))
+
+    bufs = []
+    for (m, layer, n, k, g, seed) in runs:
+        a = torch.from_numpy(synth.activations(m, k, seed=seed)).to(dev)
+        a8 = torch.empty((m, k), dtype=torch.int8, device=dev)
+        s_a = torch.empty((m,), dtype=torch.float16, device=dev)
+        y = torch.empty((m, n), dtype=torch.float16, device=dev)
+        bufs.append((a, a8, s_a, y))
+
+    nr = len(runs)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nr)] for _ in range(args.steps)]
+
+    def step(i, record=None):
+        copy = pool[i % ncopies]
+        for r, (m, layer, n, k, g, _) in enumerate(runs):
+            a, a8, s_a, y = bufs[r]
+            w4.quant_act(a, a8=a8, s_a=s_a)
+            if record is not None:
+                record[r][0].record()
+            w4.gemm(a8, s_a, copy[(layer, g)], n, k, g, y=y)
+            if record is not None:
+                record[r][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, record=ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    # per-run GEMM durations from the events around each launch
+    gemm_us = np.array([[ev[i][r][0].elapsed_time(ev[i][r][1]) * 1e3 for r in range(nr)]
+                        for i in range(args.steps)])
+    med_us = np.median(gemm_us, axis=0)
+    mean_us = gemm_us.mean(axis=0)
+    step_bytes = sum(algo_bytes(m, n, k, g) + quant_bytes(m, k) for (m, _, n, k, g, _) in runs)
+    step_ops = sum(2.0 * m * n * k for (m, _, n, k, g, _) in runs)
+    gemm_bytes = np.array([algo_bytes(m, n, k, g) for (m, _, n, k, g, _) in runs])
+    gemm_ops = np.array([2.0 * m * n * k for (m, _, n, k, g, _) in runs])
+    table = []
+    for r, (m, layer, n, k, g, _) in enumerate(runs):
+        t = med_us[r] * 1e-6
+        table.append({"m": m, "layer": layer, "n": n, "k": k, "g": g,
+                      "gemm_us_median": round(float(med_us[r]), 3),
+                      "gemm_us_mean": round(float(mean_us[r]), 3),
+                      "GBps": round(gemm_bytes[r] / t / 1e9, 1),
+                      "TOPS": round(gemm_ops[r] / t / 1e12, 2),
+                      "frac_hbm": round(gemm_bytes[r] / t / 1e9 / HBM_PEAK_GBS, 3),
+                      "frac_mfma": round(gemm_ops[r] / t / 1e12 / INT8_PEAK_TOPS, 4)})
+        log(f"{layer:8s} m={m:5d} n={n:6d} k={k:6d} g={g:4d}  gemm {med_us[r]:8.2f} us  "
+            f"{table[-1]['GBps']:8.1f} GB/s ({table[-1]['frac_hbm']:.3f} HBM)  "
+            f"{table[-1]['TOPS']:8.1f} TOPS ({table[-1]['frac_mfma']:.3f} MFMA)")
+    if args.runs_json:
+        with open(args.runs_json, "w") as f:
+            json.dump(table, f, indent=1)
+
+    # dominant kernel: the GEMM; average algorithmic bytes (or ops) per launch
+    # over average launch duration
+    avg_dur = float(mean_us.mean()) * 1e-6
+    hbm_bound = args.workload in ("llama3_8b_decode", "tiny") or max(r[0] for r in runs) <= 64
+    if hbm_bound:
+        achieved = float(gemm_bytes.mean()) / avg_dur / 1e9
+        peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
+    else:
+        achieved = float(gemm_ops.mean()) / avg_dur / 1e12
+        peak, unit, bound = INT8_PEAK_TOPS, "TFLOP/s", "mfma"
+    traffic = load_traffic() if args.workload == "llama3_8b_decode" else None
+    value_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    value_tops = step_ops / (ms_per_step * 1e-3) / 1e12
+    if hbm_bound:
+        metric_value, metric_unit = value_gbs, "GB/s"
+    else:
+        metric_value, metric_unit = value_tops, "TOPS"
+
+    result = {
+        "metric": "W4A8 GEMM TOPS + HBM GB/s vs roofline at M=1..4096 (Llama-3-8B layer shapes)",
+        "value": round(metric_value, 2),
+        "unit": metric_unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "runs": [f"M={m} {layer} N={n} K={k} g={g}" for (m, layer, n, k, g, _) in runs],
+            "step": "w4a8_quant_act + w4a8_gemm for every run",
+            "weight_rotation_copies": ncopies,
+            "parallelism": "single GPU",
+        },
+        "tops": round(value_tops, 3),
+        "gbps": round(value_gbs, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        sample_runs = [r for r in runs]
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(sample_runs, weights)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

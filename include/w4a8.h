@@ -1,0 +1,157 @@
+/*
+ * w4a8.h — C ABI of the MI355X (gfx950) W4A8 linear layer.
+ *
+ * The operation is the W4A8 GEMM of QServe/QoQ (page "[Feature] Support
+ * W4A8KV4 Quantization(QServe/QoQ)", quoted abstract): 4-bit weights reached
+ * by a progressive (two-level) quantization, 8-bit per-token activations, an
+ * 8-bit integer matrix product, and no dequantization of partial sums.
+ * The pages give no formula; this library implements the reading below.
+ *
+ *   level 1 (per output row n):  s1[n] = fp16(absmax_k |W[n,k]| / 119),
+ *                                W8 = clamp(rint(W * fp32(1/s1)), -119, 119)
+ *   level 2 (per group of g k):  s2 = max(1, ceil((hi-lo)/15)) in [1,16],
+ *                                z = rne(-lo/s2) in [0,15], with lo/hi the
+ *                                group's min/max widened to include 0,
+ *                                q = clamp(rne(W8/s2) + z, 0, 15)
+ *   decode (in the GEMM):        W8^ = (q - z) * s2, always inside int8
+ *   per-channel mode (g = K):    s1[n] = fp16((hi-lo)/15) over the row, q and z
+ *                                per row, s2 = 1
+ *   activations (per token m):   s_a[m] = fp16(absmax_k |A[m,k]| / 127),
+ *                                A8 = clamp(rint(A * fp32(1/s_a)), -127, 127)
+ *   GEMM:                        acc[m,n] = sum_k A8[m,k] * W8^[n,k]  (int32, exact)
+ *                                Y[m,n]   = fp16(acc * s_a[m] * s1[n])  (fp32 math)
+ *
+ * Conventions for every entry point
+ *   - All matrices are row-major.  W is N x K (output x input, as a linear
+ *     layer stores it), A is M x K, Y is M x N.
+ *   - fp16 values are passed as raw IEEE binary16 bit patterns (uint16_t).
+ *   - Pointers named *_dev are device (HBM) pointers; all others are host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     GPU entry points only enqueue work: they do not synchronize, allocate,
+ *     free, or keep state between calls.  The caller owns every buffer.
+ *   - Arguments are validated on the host before any HIP call.  A rejected
+ *     call returns an error status and touches no memory.  A failed kernel
+ *     launch returns W4A8_ERR_DEVICE; faults inside a kernel surface at the
+ *     caller's next synchronization, as usual for HIP.
+ *   - No entry point throws.
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A8_OK = 0,
+  W4A8_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, ld too small, misaligned */
+  W4A8_ERR_UNSUPPORTED = 2,        /* shape or group size outside what the kernels handle */
+  W4A8_ERR_BUFFER_TOO_SMALL = 3,   /* blob or workspace smaller than required */
+  W4A8_ERR_NONFINITE = 4,          /* w4a8_pack: a weight is NaN or infinite */
+  W4A8_ERR_RANGE = 5,              /* w4a8_pack: a scale overflows fp16 */
+  W4A8_ERR_LAYOUT = 6,             /* blob header magic/version/shape mismatch */
+  W4A8_ERR_DEVICE = 7              /* a HIP call failed */
+} w4a8_status;
+
+/* Group-size value that selects per-channel mode (one scale and zero per row). */
+#define W4A8_GROUP_PER_CHANNEL 0
+
+/* Shape limits.  K must be a multiple of W4A8_K_QUANTUM, N of W4A8_N_QUANTUM;
+ * K <= W4A8_K_MAX keeps every int32 accumulator exact (127*128*K < 2^31).
+ * g must be 32, 64 or 128 (and divide K), or W4A8_GROUP_PER_CHANNEL (or K). */
+#define W4A8_K_QUANTUM 128
+#define W4A8_N_QUANTUM 16
+#define W4A8_K_MAX 131072
+
+const char* w4a8_status_string(w4a8_status s);
+
+/* Text of the HIP error behind the most recent W4A8_ERR_DEVICE returned to
+ * the calling thread ("no error" if there was none).  Static storage. */
+const char* w4a8_last_device_error(void);
+
+/* ------------------------------------------------------------------ packing
+ * Packed weight blob ("layout v1").  A 256-byte header (magic, version, n, k,
+ * g) is followed by three sections at offsets that depend only on (n, k, g):
+ *   q     N*K/2 bytes: uint4 codes in the gfx950 register order.  For output
+ *         column tile t (16 rows of W) and k-block b (128 k), 1 KiB holds, for
+ *         lane l = 0..63, 16 bytes covering row 16t + (l % 16) and
+ *         k = 128b + 64h + 16(l / 16) + j  (h = 0,1; j = 0..15): dword 2h
+ *         holds j = 0..7, dword 2h+1 holds j = 8..15, and within a dword
+ *         byte i carries j = i (low nibble) and j = i + 4 (high nibble).
+ *   meta  N*(K/g) bytes: per (column tile, group, row-in-tile) one byte,
+ *         low nibble z, high nibble s2 - 1.  Per-channel mode: one group.
+ *   s1    N fp16 row scales.
+ * The blob is position independent: copy it verbatim to device memory and
+ * pass that copy to w4a8_gemm.  Device code never reads the header.       */
+
+/* Bytes of the blob for (n, k, g); 0 if the shape is unsupported. */
+size_t w4a8_packed_size(int n, int k, int g);
+
+/* Quantize W (n x k fp32, row stride ldw >= k elements) and write the blob.
+ * Host only, synchronous, thread-safe.  n_threads <= 0 uses all hardware
+ * threads; the output bytes do not depend on the thread count.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, BUFFER_TOO_SMALL, NONFINITE, RANGE. */
+w4a8_status w4a8_pack(const float* w, int n, int k, int ldw, int g,
+                      void* blob, size_t blob_bytes, int n_threads);
+
+/* Read (n, k, g) from a blob header (g is reported as W4A8_GROUP_PER_CHANNEL
+ * in per-channel mode).  Errors: INVALID_ARGUMENT, LAYOUT. */
+w4a8_status w4a8_blob_info(const void* blob, size_t blob_bytes,
+                           int* n, int* k, int* g);
+
+/* Decode a host blob back to logical arrays (for checking): q[n*k] codes,
+ * z[n*G] and s2[n*G] per group (G = k/g, or 1 per channel), s1[n] fp16 bits.
+ * Any output pointer may be NULL to skip it.  Errors: INVALID_ARGUMENT, LAYOUT. */
+w4a8_status w4a8_unpack(const void* blob, size_t blob_bytes,
+                        uint8_t* q, uint8_t* z, uint8_t* s2, uint16_t* s1);
+
+/* ----------------------------------------------------- activation quantizer
+ * Per-token int8 quantization of A (m x k fp16, row stride lda elements) into
+ * a8_dev (m x k int8, row stride lda8 bytes) and s_a_dev (m fp16 scales).
+ * m == 0 is a no-op.  k may be any positive size.  NaN/inf inputs give
+ * unspecified outputs (no device-side check).
+ * Errors: INVALID_ARGUMENT (null pointer, m < 0, k <= 0, lda < k, lda8 < k),
+ * DEVICE. */
+w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
+                           int8_t* a8_dev, int lda8, uint16_t* s_a_dev,
+                           void* stream);
+
+/* -------------------------------------------------------------- W4A8 GEMM
+ * Y = fp16(s_a[m] * s1[n] * sum_k A8[m,k] * W8^[n,k]) with int32 accumulation.
+ *   a8_dev    m x k int8, row stride lda8 bytes (lda8 >= k, lda8 % 16 == 0,
+ *             16-byte aligned)
+ *   s_a_dev   m fp16 per-token scales
+ *   blob_dev  device copy of a w4a8_pack blob for (n, k, g)
+ *   y_dev     m x n fp16 output, row stride ldy elements (ldy >= n)
+ *   acc_dev   optional (may be NULL): m x n int32 raw accumulators, row
+ *             stride ldacc elements (ldacc >= n)
+ *   workspace_dev / workspace_bytes: scratch of at least
+ *             w4a8_gemm_workspace_size(m, n, k, g) bytes (may be NULL when
+ *             that size is 0)
+ *   opts      NULL for the automatic choice; otherwise forces the kernel
+ *             variant and its split of K (tests and sweeps only).  Results
+ *             are identical for every choice.
+ * m == 0 is a no-op.  Errors: INVALID_ARGUMENT, UNSUPPORTED (k % 128, n % 16,
+ * k > W4A8_K_MAX, bad g), BUFFER_TOO_SMALL, DEVICE. */
+typedef struct {
+  int variant;   /* 0 auto, 1 skinny (intra-workgroup split-K), 2 tiled */
+  int k_split;   /* skinny: waves that share one K range (1..16), 0 = auto */
+  int reserved[6];
+} w4a8_gemm_opts;
+
+size_t w4a8_gemm_workspace_size(int m, int n, int k, int g);
+
+w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
+                      int m, const void* blob_dev, int n, int k, int g,
+                      uint16_t* y_dev, int ldy, int32_t* acc_dev, int ldacc,
+                      void* workspace_dev, size_t workspace_bytes,
+                      const w4a8_gemm_opts* opts, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

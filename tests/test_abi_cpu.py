@@ -1,0 +1,208 @@
+"""CPU tests of the C ABI library: exports, argument validation, and the host
+packer against the oracle (no GPU needed; no compute call touches HIP)."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+import w4a8_gemm_amd as w4
+from oracle import ref
+
+
+def test_library_exports_every_header_function():
+    names = w4.header_functions()
+    assert len(names) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", w4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert missing == []
+    for n in names:
+        assert hasattr(w4.lib, n)
+
+
+def test_status_strings():
+    for code in range(8):
+        assert w4.status_string(code)
+    assert w4.status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("n,k,g,ok", [
+    (256, 512, 128, True), (256, 512, 64, True), (256, 512, 32, True),
+    (256, 512, 0, True), (256, 512, 512, True),
+    (250, 512, 128, False),   # n % 16
+    (256, 500, 128, False),   # k % 128
+    (256, 512, 256, False),   # g not supported
+    (256, 512, 96, False),
+    (16, 131072, 128, True), (16, 131200, 128, False),   # K limit
+    (0, 512, 128, False), (256, 0, 128, False),
+])
+def test_packed_size_shapes(n, k, g, ok):
+    size = w4.packed_size(n, k, g)
+    assert (size > 0) == ok
+    if ok:
+        groups = 1 if g in (0, k) else k // g
+        assert size >= 256 + n * k // 2 + n * groups + 2 * n
+
+
+def _compare_with_oracle(w, g):
+    blob = w4.pack(w, g)
+    got = w4.unpack(blob)
+    want = ref.quantize_weights(w, g)
+    assert np.array_equal(got["q"], want["q"])
+    assert np.array_equal(got["z"], want["z"])
+    assert np.array_equal(got["s2"], want["s2"])
+    assert np.array_equal(got["s1"].view(np.uint16), want["s1"].view(np.uint16))
+    return blob
+
+
+@pytest.mark.parametrize("dist", ["normal", "student_t4"])
+@pytest.mark.parametrize("g", [32, 64, 128, 0])
+def test_pack_matches_oracle(dist, g):
+    w = synth.weights(128, 1024, seed=40 + g, dist=dist)
+    _compare_with_oracle(w, g)
+
+
+def test_pack_matches_oracle_special_rows():
+    w = synth.weights(64, 512, seed=77)
+    w[0] = 0.0                                  # zero row
+    w[1] = 0.0
+    w[1, 5] = 3.0                               # single outlier
+    w[2] = 0.01                                 # constant positive row
+    w[3] = -0.02                                # constant negative row
+    w[4, :] = np.linspace(-1, 1, 512)           # ramp
+    w[5, :128] = 0.0                            # zero group
+    w[6] = 1e-4                                 # subnormal fp16 scale
+    w[7] = 60000.0 * 119 / 119                  # large but finite scale
+    for g in (32, 64, 128, 0):
+        _compare_with_oracle(w, g)
+
+
+def _decode_layout(blob):
+    """Independent reader of the documented layout v1 (test-side)."""
+    n, k, g = w4.blob_info(blob)
+    groups = 1 if g == 0 else k // g
+    qsec = blob[256:256 + n * k // 2]
+    kb = k // 128
+    # reshape to [tile][kblock][lane][16 bytes]
+    chunk = qsec.reshape(n // 16, kb, 64, 16)
+    q = np.zeros((n, k), dtype=np.uint8)
+    for lane in range(64):
+        r, quarter = lane % 16, lane // 16
+        for h in range(2):
+            for j in range(16):
+                dword = 2 * h + j // 8
+                jj = j % 8
+                byte = chunk[:, :, lane, dword * 4 + jj % 4]
+                nib = (byte >> (4 * (jj // 4))) & 15
+                kk = np.arange(kb) * 128 + 64 * h + 16 * quarter + j
+                q[r::16, :][:, kk] = nib
+    meta_off = 256 + ((n * k // 2 + 255) // 256) * 256
+    meta = blob[meta_off:meta_off + n * groups].reshape(n // 16, groups, 16)
+    meta = meta.transpose(0, 2, 1).reshape(n, groups)
+    s1_off = meta_off + ((n * groups + 255) // 256) * 256
+    s1 = blob[s1_off:s1_off + 2 * n].view(np.float16)
+    return q, meta & 15, (meta >> 4) + 1, s1
+
+
+@pytest.mark.parametrize("g", [32, 128, 0])
+def test_blob_bytes_follow_documented_layout(g):
+    w = synth.weights(48, 384, seed=5)
+    blob = w4.pack(w, g)
+    q, z, s2, s1 = _decode_layout(blob)
+    want = ref.quantize_weights(w, g)
+    assert np.array_equal(q, want["q"])
+    assert np.array_equal(z, want["z"])
+    assert np.array_equal(s2, want["s2"])
+    assert np.array_equal(s1.view(np.uint16), want["s1"].view(np.uint16))
+
+
+def test_pack_deterministic_across_threads():
+    w = synth.weights(512, 1024, seed=8, dist="student_t4")
+    b1 = w4.pack(w, 64, n_threads=1)
+    b3 = w4.pack(w, 64, n_threads=3)
+    b0 = w4.pack(w, 64, n_threads=0)
+    assert np.array_equal(b1, b3) and np.array_equal(b1, b0)
+
+
+def test_pack_errors():
+    w = synth.weights(32, 256, seed=1)
+    bad = w.copy()
+    bad[3, 7] = np.nan
+    with pytest.raises(w4.W4A8Error) as e:
+        w4.pack(bad, 128)
+    assert e.value.status == 4
+    bad[3, 7] = np.inf
+    with pytest.raises(w4.W4A8Error) as e:
+        w4.pack(bad, 128)
+    assert e.value.status == 4
+    big = w.copy()
+    big[0, 0] = 3.0e38                           # absmax/119 overflows fp16
+    with pytest.raises(w4.W4A8Error) as e:
+        w4.pack(big, 128)
+    assert e.value.status == 5
+    size = w4.packed_size(32, 256, 128)
+    blob = np.empty(size, dtype=np.uint8)
+    st = w4.lib.w4a8_pack(w.ctypes.data, 32, 256, 256, 128, blob.ctypes.data, size - 1, 0)
+    assert st == 3
+    st = w4.lib.w4a8_pack(None, 32, 256, 256, 128, blob.ctypes.data, size, 0)
+    assert st == 1
+    st = w4.lib.w4a8_pack(w.ctypes.data, 32, 256, 255, 128, blob.ctypes.data, size, 0)
+    assert st == 1
+
+
+def test_unpack_rejects_bad_header():
+    w = synth.weights(32, 256, seed=1)
+    blob = w4.pack(w, 128)
+    broken = blob.copy()
+    broken[0] ^= 0xFF
+    with pytest.raises(w4.W4A8Error) as e:
+        w4.unpack(broken)
+    assert e.value.status == 6
+    with pytest.raises(w4.W4A8Error):
+        w4.unpack(blob[:100].copy())
+
+
+def test_gpu_entry_points_validate_before_any_hip_call():
+    """Every rejected argument returns its status without touching HIP."""
+    L = w4.lib
+    fake = ctypes.c_void_p(4096)          # never dereferenced: rejected first
+    # quant_act
+    assert L.w4a8_quant_act(fake, 4, 0, 8, fake, 8, fake, None) == 1      # k <= 0
+    assert L.w4a8_quant_act(fake, -1, 8, 8, fake, 8, fake, None) == 1     # m < 0
+    assert L.w4a8_quant_act(fake, 4, 8, 7, fake, 8, fake, None) == 1      # lda < k
+    assert L.w4a8_quant_act(None, 4, 8, 8, fake, 8, fake, None) == 1      # null
+    assert L.w4a8_quant_act(None, 0, 8, 8, None, 8, None, None) == 0      # m == 0: no-op
+    # gemm: (a8, lda8, s_a, m, blob, n, k, g, y, ldy, acc, ldacc, ws, ws_bytes, opts, stream)
+    args = [fake, 512, fake, 4, fake, 256, 512, 128, fake, 256, None, 0, None, 0, None, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["a8", "lda8", "s_a", "m", "blob", "n", "k", "g", "y", "ldy", "acc", "ldacc",
+                 "ws", "wsb", "opts", "stream"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return L.w4a8_gemm(*a)
+
+    assert call(n=250) == 2
+    assert call(k=500) == 2
+    assert call(g=96) == 2
+    assert call(k=131200, lda8=131200) == 2
+    assert call(m=-1) == 1
+    assert call(a8=None) == 1
+    assert call(blob=None) == 1
+    assert call(y=None) == 1
+    assert call(lda8=500) == 1
+    assert call(lda8=520) == 1                      # not a multiple of 16
+    assert call(ldy=100) == 1
+    assert call(acc=fake, ldacc=10) == 1
+    assert call(a8=ctypes.c_void_p(4104)) == 1      # misaligned
+    assert call(m=0, a8=None, s_a=None, y=None, blob=None) == 0   # empty batch
+    opts = w4.GemmOpts(7, 0)
+    assert call(opts=ctypes.byref(opts)) == 1
+    opts = w4.GemmOpts(1, 3)                         # unsupported split
+    assert call(opts=ctypes.byref(opts)) == 1
+    opts = w4.GemmOpts(1, 0)
+    assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 2   # skinny is M <= 64

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: A8, s_a and the int32 accumulators bit-exact; Y within
+1e-3 * |Y_ref| + 1 fp16 ulp of the oracle's single-rounding epilogue.
+"""
+import numpy as np
+import pytest
+
+import synth
+import w4a8_gemm_amd as w4
+from gpu_util import log, run_gemm, run_quant_act
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------ activation quantizer
+@pytest.mark.parametrize("m,k", [(1, 4096), (16, 14336), (37, 1000), (5, 8), (3, 7),
+                                 (64, 4096), (2, 24576), (300, 136)])
+def test_quant_act_bit_exact(m, k):
+    a = synth.activations(m, k, seed=m * 7 + k)
+    log(f"quant_act m={m} k={k}")
+    a8, s_a = run_quant_act(a)
+    want_a8, want_sa = ref.quant_act(a)
+    assert np.array_equal(s_a.view(np.uint16), want_sa.view(np.uint16))
+    assert np.array_equal(a8, want_a8)
+
+
+def test_quant_act_exhaustive_fp16_scales():
+    """Every positive finite fp16 absmax, one token each, bit-exact."""
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    alpha = bits.view(np.float16)
+    rng = np.random.default_rng(3)
+    frac = rng.uniform(-1, 1, size=(alpha.size, 63)).astype(np.float32)
+    a = np.empty((alpha.size, 64), dtype=np.float16)
+    a[:, 0] = alpha
+    a[:, 1:] = (frac * alpha.astype(np.float32)[:, None]).astype(np.float16)
+    log(f"quant_act exhaustive scales m={alpha.size}")
+    a8, s_a = run_quant_act(a)
+    want_a8, want_sa = ref.quant_act(a)
+    assert np.array_equal(s_a.view(np.uint16), want_sa.view(np.uint16))
+    assert np.array_equal(a8, want_a8)
+
+
+def test_quant_act_zero_rows_and_ties():
+    a = np.zeros((4, 256), dtype=np.float16)
+    a[1, :8] = [127, 2.5, -3.5, 0.5, -0.5, 1.5, 0, -127]
+    a[2, 100] = -65504.0
+    a[3, :] = 1e-7
+    log("quant_act zero rows and ties")
+    a8, s_a = run_quant_act(a)
+    want_a8, want_sa = ref.quant_act(a)
+    assert np.array_equal(s_a.view(np.uint16), want_sa.view(np.uint16))
+    assert np.array_equal(a8, want_a8)
+    assert not a8[0].any() and float(s_a[0]) == 0
+
+
+def test_quant_act_strided_rows():
+    import torch
+    dev = torch.device("cuda:0")
+    a_full = synth.activations(9, 520, seed=5)
+    a = torch.from_numpy(a_full).to(dev)[:, :512]          # lda = 520 > k
+    a8 = torch.zeros((9, 528), dtype=torch.int8, device=dev)
+    s_a = torch.empty(9, dtype=torch.float16, device=dev)
+    log("quant_act strided lda=520 lda8=528")
+    w4.quant_act(a, a8=a8[:, :512], s_a=s_a)
+    torch.cuda.synchronize()
+    want_a8, want_sa = ref.quant_act(a_full[:, :512])
+    assert np.array_equal(a8[:, :512].cpu().numpy(), want_a8)
+    assert not a8[:, 512:].cpu().numpy().any()              # padding untouched
+    assert np.array_equal(s_a.cpu().numpy().view(np.uint16), want_sa.view(np.uint16))
+
+
+# ------------------------------------------------------------ GEMM, whole outputs
+SMALL = [
+    # m, n, k, g, dist
+    (16, 256, 512, 128, "normal"),          # the tiny workload
+    (1, 48, 384, 64, "normal"),
+    (3, 272, 640, 32, "student_t4"),
+    (17, 80, 1024, 128, "normal"),
+    (33, 112, 256, 0, "student_t4"),
+    (64, 512, 1152, 128, "normal"),
+    (65, 320, 512, 128, "normal"),
+    (100, 1040, 768, 64, "student_t4"),
+    (130, 48, 128, 32, "normal"),
+    (256, 512, 1024, 0, "normal"),
+]
+
+
+def _layer(m, n, k, g, dist, seed):
+    w = synth.weights(n, k, seed=seed, dist=dist)
+    a = synth.activations(m, k, seed=seed + 1)
+    return w, a, ref.linear(a, w, g)
+
+
+@pytest.mark.parametrize("m,n,k,g,dist", SMALL)
+def test_gemm_auto_bit_exact(m, n, k, g, dist):
+    w, a, out = _layer(m, n, k, g, dist, seed=m + n + k + g)
+    blob = w4.pack(w, g)
+    log(f"gemm auto m={m} n={n} k={k} g={g}")
+    y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g)
+    assert np.array_equal(acc, out["acc"])
+    assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
+@pytest.mark.parametrize("k_split", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("m,n,k,g", [(16, 256, 512, 128), (5, 96, 1152, 32), (40, 64, 384, 0)])
+def test_gemm_skinny_every_split_identical(m, n, k, g, k_split):
+    w, a, out = _layer(m, n, k, g, "normal", seed=11 + m)
+    blob = w4.pack(w, g)
+    mr = 1 if m <= 16 else (2 if m <= 32 else 4)
+    assert k_split * mr <= 64                      # n < 32768: one column tile per wave
+    log(f"gemm skinny m={m} n={n} k={k} g={g} k_split={k_split}")
+    y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=1, k_split=k_split)
+    assert np.array_equal(acc, out["acc"])
+    assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 128), (48, 96, 640, 64), (64, 4096, 512, 32)])
+def test_gemm_tiled_on_small_m(m, n, k, g):
+    w, a, out = _layer(m, n, k, g, "student_t4", seed=90 + m)
+    blob = w4.pack(w, g)
+    log(f"gemm tiled m={m} n={n} k={k} g={g}")
+    y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=2)
+    assert np.array_equal(acc, out["acc"])
+    assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
+def test_gemm_extreme_operands():
+    """A8 = +-127 and decoded weights at the int8 extremes over the deepest K."""
+    n, k, g = 32, 24576, 128
+    w = np.zeros((n, k), dtype=np.float32)
+    w[0::2] = 1.0                                   # W8 = 119 everywhere
+    w[1::2] = -1.0
+    w[2, :] = np.tile(np.array([-1.0, 1.0], np.float32), k // 2)
+    blob = w4.pack(w, g)
+    qw = ref.quantize_weights(w, g)
+    w8hat = ref.decoded_weights(qw)
+    a8 = np.full((3, k), 127, dtype=np.int8)
+    a8[1] = -127
+    a8[2, ::2] = -127
+    s_a = np.ones(3, dtype=np.float16) * np.float16(2 ** -10)
+    acc_ref = ref.gemm_acc(a8, w8hat)
+    log("gemm extreme operands k=24576")
+    y, acc = run_gemm(a8, s_a, blob, n, k, g)
+    assert np.array_equal(acc, acc_ref)
+
+
+def test_gemm_zero_token_and_strided_output():
+    import torch
+    m, n, k, g = 20, 160, 512, 64
+    w, a, out = _layer(m, n, k, g, "normal", seed=123)
+    a = a.copy()
+    a[4] = 0
+    out = ref.linear(a, w, g)
+    blob = w4.pack(w, g)
+    dev = torch.device("cuda:0")
+    a8 = torch.zeros((m, k + 32), dtype=torch.int8, device=dev)
+    a8[:, :k] = torch.from_numpy(out["a8"]).to(dev)
+    s_a = torch.from_numpy(out["s_a"]).to(dev)
+    y = torch.full((m, n + 8), -1.0, dtype=torch.float16, device=dev)
+    acc = torch.zeros((m, n + 4), dtype=torch.int32, device=dev)
+    wdev = w4.to_device(blob, dev)
+    log("gemm strided lda8/ldy/ldacc with a zero token")
+    w4.gemm(a8[:, :k], s_a, wdev, n, k, g, y=y[:, :n], acc=acc[:, :n])
+    torch.cuda.synchronize()
+    y_np, acc_np = y.cpu().numpy(), acc.cpu().numpy()
+    assert np.array_equal(acc_np[:, :n], out["acc"])
+    assert ref.y_tolerance_ok(y_np[:, :n], out["y"]).all()
+    assert (y_np[:, n:] == -1.0).all() and not acc_np[:, n:].any()
+    assert not y_np[4, :n].any()
+
+
+def test_gemm_empty_batch_is_noop():
+    import torch
+    dev = torch.device("cuda:0")
+    w = synth.weights(64, 256, seed=1)
+    blob = w4.to_device(w4.pack(w, 128), dev)
+    a8 = torch.zeros((0, 256), dtype=torch.int8, device=dev)
+    s_a = torch.zeros((0,), dtype=torch.float16, device=dev)
+    y = w4.gemm(a8, s_a, blob, 64, 256, 128)
+    assert tuple(y.shape) == (0, 64)
+
+
+# ------------------------------------------------------------ full sizes, sampled
+def _full_runs():
+    runs = []
+    for cfg_idx, (name, items) in enumerate(synth.workloads().items()):
+        if name == "tiny":
+            continue
+        layers = {}
+        for (_, m, layer, n, k, g, dist) in items:
+            layers.setdefault((layer, n, k, g, dist), []).append(m)
+        for shape_idx, (key, ms) in enumerate(layers.items()):
+            runs.append(pytest.param(cfg_idx, shape_idx, key, ms, id=f"{name}-{key[0]}-g{key[3]}"))
+    return runs
+
+
+@pytest.mark.parametrize("cfg_idx,shape_idx,key,ms", _full_runs())
+def test_gemm_full_size_sampled(cfg_idx, shape_idx, key, ms):
+    """Every full-size run: whole A8/s_a bit-exact, acc bit-exact and Y within
+    tolerance on 64 sampled columns (plus the first and last), all rows."""
+    import torch
+    layer, n, k, g, dist = key
+    dev = torch.device("cuda:0")
+    w = synth.weights(n, k, seed=synth.weight_seed(cfg_idx, shape_idx, 0), dist=dist)
+    blob = w4.pack(w, g)
+    wdev = w4.to_device(blob, dev)
+    rng = np.random.default_rng(cfg_idx * 100 + shape_idx)
+    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 64, replace=False)]))
+    qw = ref.quantize_weights(w[cols], g)
+    del w
+    w8hat = ref.decoded_weights(qw)
+    for mi, m in enumerate(ms):
+        a = synth.activations(m, k, seed=synth.act_seed(cfg_idx, shape_idx, mi))
+        log(f"full-size {layer} m={m} n={n} k={k} g={g}")
+        a_dev = torch.from_numpy(a).to(dev)
+        a8, s_a = w4.quant_act(a_dev)
+        y, acc = w4.gemm(a8, s_a, wdev, n, k, g, want_acc=True)
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(cols).to(dev)
+        y_s = y.index_select(1, idx).cpu().numpy()
+        acc_s = acc.index_select(1, idx).cpu().numpy()
+        a8_np, s_a_np = a8.cpu().numpy(), s_a.cpu().numpy()
+        del y, acc, a8, s_a, a_dev
+        want_a8, want_sa = ref.quant_act(a)
+        assert np.array_equal(s_a_np.view(np.uint16), want_sa.view(np.uint16))
+        assert np.array_equal(a8_np, want_a8)
+        acc_ref = ref.gemm_acc(want_a8, w8hat)
+        assert np.array_equal(acc_s, acc_ref)
+        y_ref = ref.epilogue(acc_ref, want_sa, qw["s1"])
+        assert ref.y_tolerance_ok(y_s, y_ref).all()
