@@ -81,8 +81,9 @@ const char* w4a8_last_device_error(void);
  *         k = 128b + 64h + 16(l / 16) + j  (h = 0,1; j = 0..15): dword 2h
  *         holds j = 0..7, dword 2h+1 holds j = 8..15, and within a dword
  *         byte i carries j = i (low nibble) and j = i + 4 (high nibble).
- *   meta  N*(K/g) bytes: per (column tile, group, row-in-tile) one byte,
- *         low nibble z, high nibble s2 - 1.  Per-channel mode: one group.
+ *   meta  N*G4 bytes, G4 = (groups per row) rounded up to a multiple of 4:
+ *         row n holds one byte per group (low nibble z, high nibble s2 - 1)
+ *         at n*G4 + group; padding bytes are 0.  Per-channel mode: 1 group.
  *   s1    N fp16 row scales.
  * The blob is position independent: copy it verbatim to device memory and
  * pass that copy to w4a8_gemm.  Device code never reads the header.       */
@@ -138,8 +139,9 @@ w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
  * k > W4A8_K_MAX, bad g), BUFFER_TOO_SMALL, DEVICE. */
 typedef struct {
   int variant;   /* 0 auto, 1 skinny (intra-workgroup split-K), 2 tiled */
-  int k_split;   /* skinny: waves that share one K range (1..16), 0 = auto */
-  int reserved[6];
+  int k_split;   /* skinny: waves that share one K range (1..8), 0 = auto */
+  int n_tiles;   /* skinny: 16-column tiles per wave (1, 2 or 4), 0 = auto */
+  int reserved[5];
 } w4a8_gemm_opts;
 
 size_t w4a8_gemm_workspace_size(int m, int n, int k, int g);

@@ -44,7 +44,7 @@ def test_packed_size_shapes(n, k, g, ok):
     assert (size > 0) == ok
     if ok:
         groups = 1 if g in (0, k) else k // g
-        assert size >= 256 + n * k // 2 + n * groups + 2 * n
+        assert size >= 256 + n * k // 2 + n * ((groups + 3) // 4 * 4) + 2 * n
 
 
 def _compare_with_oracle(w, g):
@@ -100,9 +100,11 @@ def _decode_layout(blob):
                 kk = np.arange(kb) * 128 + 64 * h + 16 * quarter + j
                 q[r::16, :][:, kk] = nib
     meta_off = 256 + ((n * k // 2 + 255) // 256) * 256
-    meta = blob[meta_off:meta_off + n * groups].reshape(n // 16, groups, 16)
-    meta = meta.transpose(0, 2, 1).reshape(n, groups)
-    s1_off = meta_off + ((n * groups + 255) // 256) * 256
+    g4 = (groups + 3) // 4 * 4
+    meta = blob[meta_off:meta_off + n * g4].reshape(n, g4)
+    assert not meta[:, groups:].any()           # padding is zero
+    meta = meta[:, :groups]
+    s1_off = meta_off + ((n * g4 + 255) // 256) * 256
     s1 = blob[s1_off:s1_off + 2 * n].view(np.float16)
     return q, meta & 15, (meta >> 4) + 1, s1
 
@@ -202,7 +204,7 @@ def test_gpu_entry_points_validate_before_any_hip_call():
     assert call(m=0, a8=None, s_a=None, y=None, blob=None) == 0   # empty batch
     opts = w4.GemmOpts(7, 0)
     assert call(opts=ctypes.byref(opts)) == 1
-    opts = w4.GemmOpts(1, 3)                         # unsupported split
+    opts = w4.GemmOpts(1, 9)                         # unsupported split (> 8 waves)
     assert call(opts=ctypes.byref(opts)) == 1
     opts = w4.GemmOpts(1, 0)
     assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 2   # skinny is M <= 64

@@ -3,6 +3,7 @@
 // pack.cpp.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "../../include/w4a8.h"
@@ -29,23 +30,33 @@ bool gemm_shape_supported(int n, int k, int g) {
   return (g == 32 || g == 64 || g == 128) && k % g == 0;
 }
 
-// Automatic choice of kernel and split.  The skinny kernel covers M <= 64:
-// it keeps every weight byte in flight early and splits K across the waves
-// of a workgroup so that even the narrowest layers put thousands of waves on
-// the 256 compute units.
+// K blocks per wave for a given split: a multiple of the kernel's ring
+// depth (4), so that every wave starts on a meta dword.
+int blocks_per_wave(int kblocks, int kw) { return ((kblocks + kw - 1) / kw + 3) / 4 * 4; }
+
+// Automatic choice for the skinny kernel (M <= 64), from rocprofv3 sweeps on
+// MI355X over the Llama-3-8B decode shapes.  Narrow layers (<= 256 column
+// tiles) need every wave they can get, so K is split over 8 waves and each
+// wave keeps one column tile; wider layers give each wave 2 (or, for
+// 5..16 tokens, 4) column tiles so that the activation fragments loaded per
+// block serve more weights.
 SkinnyConfig choose_skinny(int m, int n, int k) {
   SkinnyConfig c;
   c.mr = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   const int ntiles = n / kColTile;
-  c.nc = ntiles >= 2048 ? 2 : 1;
-  if (c.mr == 4) c.nc = 1;
-  const int wgs = (ntiles + c.nc - 1) / c.nc;
   const int kblocks = k / kKBlock;
-  // aim for ~8 waves per CU (256 CUs), at least 2 k-blocks per wave
-  int kw = 1;
-  while (kw < 16 && wgs * kw < 2048 && kblocks / (kw * 2) >= 2) kw *= 2;
-  while (kw * c.mr * c.nc > 64) kw /= 2;
-  c.kw = kw;
+  int kw = 8;
+  if (ntiles <= 256) {
+    c.nc = 1;
+  } else if (ntiles <= 1024 || c.mr > 1 || m <= 4) {
+    c.nc = 2;
+  } else {
+    c.nc = 4;
+    kw = 4;
+  }
+  kw = std::min(kw, std::max(1, kblocks / 4));
+  c.kbw = blocks_per_wave(kblocks, kw);
+  c.kw = (kblocks + c.kbw - 1) / c.kbw;
   return c;
 }
 
@@ -109,9 +120,9 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
   p.s1 = reinterpret_cast<const uint16_t*>(base + sec.s1_off);
   p.n = n;
   p.k = k;
-  p.groups = sec.groups;
-  const int ge = effective_group(k, g);
-  p.gpb_shift = ge == k ? -1 : (ge == 128 ? 0 : (ge == 64 ? 1 : 2));
+  p.meta_row_bytes = sec.meta_row_bytes;
+  p.kb_per_wave = 0;
+  const int gpb = groups_per_block(k, g);
   p.y = y_dev;
   p.ldy = ldy;
   p.acc = acc_dev;
@@ -125,15 +136,19 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
   if (variant == 1) {
     if (m > 64) return W4A8_ERR_UNSUPPORTED;
     SkinnyConfig c = choose_skinny(m, n, k);
-    if (opts && opts->k_split > 0) c.kw = opts->k_split;
-    if (!skinny_config_supported(c)) return W4A8_ERR_INVALID_ARGUMENT;
-    e = launch_gemm_skinny(p, c, s);
+    if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
+    if (opts && opts->k_split > 0) {
+      c.kw = opts->k_split;
+      c.kbw = blocks_per_wave(k / kKBlock, c.kw);
+    }
+    if (!skinny_config_supported(c, k, gpb)) return W4A8_ERR_INVALID_ARGUMENT;
+    e = launch_gemm_skinny(p, gpb, c, s);
   } else {
     TiledConfig c;
     c.mr = 4;
     c.nc = (n / kColTile) >= 1024 ? 4 : 2;
     c.nw = 4;
-    e = launch_gemm_tiled(p, c, s);
+    e = launch_gemm_tiled(p, gpb, c, s);
   }
   return device_status(e);
 }

@@ -15,18 +15,25 @@ struct GemmParams {
   const uint8_t* meta;   // meta section
   const uint16_t* s1;    // s1 section
   int n, k;
-  int groups;            // groups per row (K / g, or 1 per channel)
-  int gpb_shift;         // log2(groups per 128-k block) for g in {128,64,32}; -1 per channel
+  int meta_row_bytes;    // meta bytes per output row (groups rounded up to 4)
   uint16_t* y;
   int ldy;
   int32_t* acc;          // optional raw accumulators
   int ldacc;
+  int kb_per_wave;       // skinny: 128-k blocks per wave (a multiple of 4 / groups-per-block)
 };
 
+// Groups per 128-k block: 1, 2 or 4 for g = 128, 64, 32; 0 in per-channel mode.
+inline int groups_per_block(int k, int g) {
+  if (g == 0 || g == k) return 0;
+  return 128 / g;
+}
+
 struct SkinnyConfig {
-  int mr;   // 16-row tiles per workgroup (1, 2 or 4)
-  int nc;   // 16-column tiles per wave (1, 2 or 4)
-  int kw;   // waves splitting K inside one workgroup (1..16)
+  int mr;    // 16-row tiles per workgroup (1, 2 or 4)
+  int nc;    // 16-column tiles per wave (1 or 2)
+  int kw;    // waves splitting K inside one workgroup (1..8)
+  int kbw;   // 128-k blocks per wave
 };
 
 struct TiledConfig {
@@ -37,9 +44,11 @@ struct TiledConfig {
 
 hipError_t launch_quant_act(const uint16_t* a, int m, int k, int lda, int8_t* a8, int lda8,
                             uint16_t* s_a, hipStream_t stream);
-hipError_t launch_gemm_skinny(const GemmParams& p, const SkinnyConfig& c, hipStream_t stream);
-hipError_t launch_gemm_tiled(const GemmParams& p, const TiledConfig& c, hipStream_t stream);
-bool skinny_config_supported(const SkinnyConfig& c);
+hipError_t launch_gemm_skinny(const GemmParams& p, int gpb, const SkinnyConfig& c,
+                              hipStream_t stream);
+hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
+                             hipStream_t stream);
+bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb);
 bool tiled_config_supported(const TiledConfig& c);
 
 }  // namespace w4a8

@@ -29,17 +29,19 @@ struct Sections {
   size_t meta_off, meta_bytes;
   size_t s1_off, s1_bytes;
   size_t total;
-  int groups;  // groups per row
+  int groups;         // groups per row
+  int meta_row_bytes; // groups per row rounded up to a multiple of 4
 };
 
 inline Sections sections(int n, int k, int g) {
   Sections s;
   int ge = effective_group(k, g);
   s.groups = k / ge;
+  s.meta_row_bytes = (s.groups + 3) & ~3;
   s.q_off = kHeaderBytes;
   s.q_bytes = size_t(n) * size_t(k) / 2;
   s.meta_off = s.q_off + align256(s.q_bytes);
-  s.meta_bytes = size_t(n) * size_t(s.groups);
+  s.meta_bytes = size_t(n) * size_t(s.meta_row_bytes);
   s.s1_off = s.meta_off + align256(s.meta_bytes);
   s.s1_bytes = size_t(n) * 2;
   s.total = s.s1_off + align256(s.s1_bytes);
@@ -58,9 +60,11 @@ inline void q_position(int n, int k, int kblocks, size_t* byte, int* nibble) {
   *nibble = jj / 4;
 }
 
-// Byte offset (inside the meta section) of group `grp` of row n.
-inline size_t meta_position(int n, int grp, int groups) {
-  return (size_t(n / kColTile) * groups + grp) * kColTile + (n % kColTile);
+// Byte offset (inside the meta section) of group `grp` of row n: one row of
+// meta bytes per output row, padded to whole dwords so that a lane can fetch
+// four consecutive groups of its row with one 32-bit load.
+inline size_t meta_position(int n, int grp, int meta_row_bytes) {
+  return size_t(n) * size_t(meta_row_bytes) + size_t(grp);
 }
 
 }  // namespace w4a8

@@ -204,7 +204,7 @@ extern "C" w4a8_status w4a8_pack(const float* w, int n, int k, int ldw, int g, v
         }
         s1sec[row] = s1b;
         for (int gi = 0; gi < groups; ++gi)
-          msec[meta_position(row, gi, groups)] = uint8_t((z[gi] & 15u) | ((s2[gi] - 1u) << 4));
+          msec[meta_position(row, gi, sec.meta_row_bytes)] = uint8_t((z[gi] & 15u) | ((s2[gi] - 1u) << 4));
         for (int kk = 0; kk < k; ++kk) {
           size_t byte;
           int nib;
@@ -275,7 +275,7 @@ extern "C" w4a8_status w4a8_unpack(const void* blob, size_t blob_bytes, uint8_t*
       }
     }
     for (int gi = 0; gi < sec.groups; ++gi) {
-      uint8_t mb = msec[meta_position(row, gi, sec.groups)];
+      uint8_t mb = msec[meta_position(row, gi, sec.meta_row_bytes)];
       if (z) z[size_t(row) * sec.groups + gi] = uint8_t(mb & 15u);
       if (s2) s2[size_t(row) * sec.groups + gi] = uint8_t((mb >> 4) + 1u);
     }
