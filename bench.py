@@ -29,7 +29,9 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
-GEMM_SRC = os.path.join(ROOT, "w4a8_gemm_amd", "csrc", "gemm.hip")
+# counters are keyed to the kernels they were taken on
+GEMM_SRCS = [os.path.join(ROOT, "w4a8_gemm_amd", "csrc", f)
+             for f in ("skinny.hip", "gemm_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
@@ -48,8 +50,11 @@ def log(msg):
 
 
 def gemm_source_hash():
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic():
@@ -65,7 +70,51 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(runs, weights, budget_s=20.0):
+class HipEvent:
+    """A HIP event created with hipEventDisableSystemFence, recorded on a given
+    stream.  Timing-only events without the system-scope cache writeback and
+    invalidate that a default event performs, so the interval between two of
+    them is closer to the kernel in between.  Uses the HIP runtime torch has
+    already loaded (same process-wide runtime as the library)."""
+    _lib = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def lib(cls):
+        if cls._lib is None:
+            import ctypes
+            import torch
+            path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            cls._lib = h
+        return cls._lib
+
+    def __init__(self):
+        import ctypes
+        self.h = ctypes.c_void_p()
+        st = self.lib().hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream_ptr):
+        st = self.lib().hipEventRecord(self.h, stream_ptr)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        st = self.lib().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+
+def cpu_baseline(runs, weights, budget_s=15.0):
     """The oracle, untuned, on a bounded sample of the same workload: every
     run, restricted to the first `cols` output columns of each layer."""
     from oracle import ref
@@ -74,7 +123,7 @@ def cpu_baseline(runs, weights, budget_s=20.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    cols = 512
+    cols = 2048
     qws = {}
     for (layer, n, k, g), w in weights.items():
         qws[layer] = ref.quantize_weights(w[:cols], g)      # offline pack: not timed
@@ -93,7 +142,7 @@ def cpu_baseline(runs, weights, budget_s=20.0):
             ref.epilogue(acc, s_a, qws[layer]["s1"])
             done_bytes += algo_bytes(m, cols, k, g) + quant_bytes(m, k)
         passes += 1
-        if time.perf_counter() - t0 >= budget_s or passes >= 50:
+        if time.perf_counter() - t0 >= budget_s or passes >= 200:
             break
     dt = time.perf_counter() - t0
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
@@ -112,6 +161,8 @@ def main():
     ap.add_argument("--rotation-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--runs-json", default="")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step (reported as context)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -140,7 +191,7 @@ def main():
         w = synth.weights(n, k, seed=synth.weight_seed(cfg_idx, shape_idx, 0), dist=dist)
         blobs[(layer, g)] = w4.to_device(w4.pack(w, g), dev)
         if not args.no_cpu_baseline:
-            weights[(layer, n, k, g)] = w[:512].copy()
+            weights[(layer, n, k, g)] = w[:2048].copy()
         del w
     per_copy = sum(b.numel() for b in blobs.values())
     ncopies = max(2, int(np.ceil(args.rotation_gib * 2 ** 30 / per_copy)))
@@ -163,38 +214,75 @@ def main():
         bufs.append((a, a8, s_a, y))
 
     nr = len(runs)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nr)] for _ in range(args.steps)]
 
-    def step(i, record=None):
-        copy = pool[i % ncopies]
+    stream_ptr = int(torch.cuda.current_stream().cuda_stream)
+
+    def launch_step(copy, record=None):
         for r, (m, layer, n, k, g, _) in enumerate(runs):
             a, a8, s_a, y = bufs[r]
             w4.quant_act(a, a8=a8, s_a=s_a)
             if record is not None:
-                record[r][0].record()
+                record[r][0].record(stream_ptr)
             w4.gemm(a8, s_a, copy[(layer, g)], n, k, g, y=y)
             if record is not None:
-                record[r][1].record()
+                record[r][1].record(stream_ptr)
 
+    def new_events():
+        return [(HipEvent(), HipEvent()) for _ in range(nr)]
+
+    # Timed region: `steps` steps enqueued from the host behind a GPU spin
+    # kernel, so that the whole region is already queued when the GPU reaches
+    # it and the host's launch rate never starves the GPU.  Events recorded on
+    # the launch stream around each GEMM give its on-GPU duration.
+    events = [new_events() for _ in range(args.steps)]
     for i in range(args.warmup):
-        step(i)
+        launch_step(pool[i % ncopies])
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record()
+    t_start, t_end = HipEvent(), HipEvent()
+    spin_s = max(0.02, 5e-5 * args.steps * nr)
+    torch.cuda._sleep(int(2.4e9 * spin_s))          # GPU spin while the host enqueues
+    t_start.record(stream_ptr)
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, record=ev[i])
-    t_end.record()
+        launch_step(pool[i % ncopies], record=events[i])
+    t_end.record(stream_ptr)
+    enqueue_s = time.perf_counter() - wall0
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    per_step_gemm = [[events[i][r][0].elapsed_time(events[i][r][1]) for r in range(nr)]
+                     for i in range(args.steps)]
+    log(f"host enqueue {enqueue_s * 1e3:.1f} ms, GPU spin ~{spin_s * 1e3:.0f} ms, "
+        f"timed GPU region {total_ms:.2f} ms")
+    if enqueue_s * 1e3 > total_ms + 1e3 * spin_s:
+        log("warning: the host enqueue outlasted the GPU spin; the GPU may have idled")
 
-    # per-run GEMM durations from the events around each launch
-    gemm_us = np.array([[ev[i][r][0].elapsed_time(ev[i][r][1]) * 1e3 for r in range(nr)]
-                        for i in range(args.steps)])
+    # Context: the same steps replayed as HIP graphs (no events, no host
+    # launches in between), one graph per weight copy.
+    ms_per_step_graph = None
+    if not args.no_graph:
+        try:
+            graphs = []
+            for i in range(ncopies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    launch_step(pool[i])
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % ncopies].replay()
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record()
+            for i in range(args.steps):
+                graphs[i % ncopies].replay()
+            g1.record()
+            torch.cuda.synchronize()
+            ms_per_step_graph = g0.elapsed_time(g1) / args.steps
+        except Exception as e:
+            log(f"graph replay unavailable: {e}")
+
+    gemm_us = np.array(per_step_gemm) * 1e3
     med_us = np.median(gemm_us, axis=0)
     mean_us = gemm_us.mean(axis=0)
     step_bytes = sum(algo_bytes(m, n, k, g) + quant_bytes(m, k) for (m, _, n, k, g, _) in runs)
@@ -254,11 +342,13 @@ def main():
             "runs": [f"M={m} {layer} N={n} K={k} g={g}" for (m, layer, n, k, g, _) in runs],
             "step": "w4a8_quant_act + w4a8_gemm for every run",
             "weight_rotation_copies": ncopies,
+            "launch": "host-enqueued behind a GPU spin, events around every GEMM",
             "parallelism": "single GPU",
         },
         "tops": round(value_tops, 3),
         "gbps": round(value_gbs, 2),
-        "wall_s_timed": round(wall, 3),
+        "ms_per_step_graph_replay": (round(ms_per_step_graph, 4)
+                                     if ms_per_step_graph is not None else None),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
     }

@@ -1,0 +1,127 @@
+// Device-side pieces shared by the W4A8 GEMM kernels (gfx950): the
+// in-register decode of 4-bit codes to int8 MFMA operands, fp16 helpers and
+// the scale epilogue.
+//
+// The decode of 4-bit codes to the int8 MFMA operand happens in registers
+// with integer operations only (the progressive-quantization point of the
+// QServe/QoQ abstract; the LiquidGEMM digest, section "Метод", sets the bar
+// of a couple of arithmetic operations per four weights).  Per 32-bit word of
+// packed codes (eight weights):
+//     lo = w & 0x0F0F0F0F,  hi = (w >> 4) & 0x0F0F0F0F        (4 codes each)
+//     b  = pk_mad_u16(x, s2|s2<<16, c*0x01010101) ^ 0x80808080
+// with c = 128 - z*s2.  Each byte of pk_mad is q*s2 + 128 - z*s2 =
+// (q - z)*s2 + 128, which lies in [0, 255] because the packer guarantees the
+// decoded weight is inside int8, so no carry crosses a byte and the xor turns
+// the biased byte into the two's-complement int8 (q - z)*s2.  That is 7 VALU
+// operations per 8 weights, plus 7 per lane and group for the constants.
+//
+// int8 MFMA v_mfma_i32_16x16x64_i8 accumulates exactly in int32 over all of K
+// (no per-group rescale of partial sums, because s2 and z are folded into the
+// int8 operand).  Operand mapping (lane l of a wave):
+//   A (activations): row l % 16, k = kbase + 16*(l/16) + [0..15]
+//   B (weights):     column l % 16, same k; both operands use the same k order
+//   D:               lane l, register r holds row 4*(l/16) + r, column l % 16
+//
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace w4a8 {
+namespace dev {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
+  u16x2 va = __builtin_bit_cast(u16x2, a);
+  u16x2 vb = __builtin_bit_cast(u16x2, b);
+  u16x2 vc = __builtin_bit_cast(u16x2, c);
+  return __builtin_bit_cast(uint32_t, (u16x2)(va * vb + vc));
+}
+
+struct GroupConst {
+  uint32_t s2s2;  // s2 in both 16-bit halves
+  uint32_t cccc;  // (128 - z*s2) in all four bytes
+};
+
+__device__ __forceinline__ GroupConst group_const(uint32_t mb) {
+  GroupConst g;
+  uint32_t s2 = (mb >> 4) + 1u;
+  uint32_t z = mb & 15u;
+  g.s2s2 = s2 | (s2 << 16);
+  uint32_t c = 128u - __umul24(z, s2);
+  g.cccc = __builtin_amdgcn_perm(0u, c, 0u);  // replicate byte 0
+  return g;
+}
+
+__device__ __forceinline__ uint32_t dec4(uint32_t nibbles, GroupConst g) {
+  return pk_mad_u16(nibbles, g.s2s2, g.cccc) ^ 0x80808080u;
+}
+
+// Two packed words (16 codes) -> one B operand (16 int8, k order j = 0..15).
+__device__ __forceinline__ v4i decode16(uint32_t w0, uint32_t w1, GroupConst g) {
+  v4i b;
+  b[0] = int(dec4(w0 & 0x0F0F0F0Fu, g));
+  b[1] = int(dec4((w0 >> 4) & 0x0F0F0F0Fu, g));
+  b[2] = int(dec4(w1 & 0x0F0F0F0Fu, g));
+  b[3] = int(dec4((w1 >> 4) & 0x0F0F0F0Fu, g));
+  return b;
+}
+
+__device__ __forceinline__ uint16_t f2h_bits(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Epilogue scales of one lane, fetched at kernel start so that the final
+// stores do not wait on a dependent global load.
+template <int MR, int NC>
+struct EpiScales {
+  float s1[NC];      // column (tile0 + c) * 16 + lane % 16
+  float sa[MR][4];   // rows (row_tile0 + i) * 16 + 4 * (lane / 16) + r
+};
+
+template <int MR, int NC>
+__device__ __forceinline__ EpiScales<MR, NC> load_scales(const GemmParams& p, int row_tile0,
+                                                         int tile0, int lane) {
+  EpiScales<MR, NC> e;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) e.s1[c] = h2f(p.s1[min((tile0 + c) * 16 + (lane & 15), p.n - 1)]);
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      e.sa[i][r] = h2f(p.s_a[min((row_tile0 + i) * 16 + 4 * (lane >> 4) + r, p.m - 1)]);
+  return e;
+}
+
+// Store one 16x16 accumulator fragment (4 values per lane) with the epilogue
+// Y = fp16((acc * s_a) * s1) in fp32.
+__device__ __forceinline__ void store_frag(const GemmParams& p, int row0, int col0, int lane,
+                                           const int32_t v[4], float s1, const float sa[4]) {
+  const int col = col0 + (lane & 15);
+  if (col >= p.n) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + 4 * (lane >> 4) + r;
+    if (row < p.m) {
+      const float y = (static_cast<float>(v[r]) * sa[r]) * s1;
+      p.y[size_t(row) * p.ldy + col] = f2h_bits(y);
+      if (p.acc) p.acc[size_t(row) * p.ldacc + col] = v[r];
+    }
+  }
+}
+
+// Meta byte of group `grp` for a lane whose row pointer is mrow.
+__device__ __forceinline__ uint32_t meta_byte(const uint8_t* mrow, int grp) {
+  return mrow[grp];
+}
+
+}  // namespace dev
+}  // namespace w4a8
