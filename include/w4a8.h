@@ -140,8 +140,9 @@ w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
 typedef struct {
   int variant;   /* 0 auto, 1 skinny (intra-workgroup split-K), 2 tiled */
   int k_split;   /* skinny: waves that share one K range (1..8), 0 = auto */
-  int n_tiles;   /* skinny: 16-column tiles per wave (1, 2 or 4), 0 = auto */
-  int reserved[5];
+  int n_tiles;   /* 16-column tiles per wave: skinny 1, 2 or 4; tiled 2 or 4; 0 = auto */
+  int m_tiles;   /* tiled: 16-row tiles per workgroup (4 or 8), 0 = auto */
+  int reserved[4];
 } w4a8_gemm_opts;
 
 size_t w4a8_gemm_workspace_size(int m, int n, int k, int g);

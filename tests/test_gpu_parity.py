@@ -116,14 +116,36 @@ def test_gemm_skinny_every_split_identical(m, n, k, g, k_split):
     assert ref.y_tolerance_ok(y, out["y"]).all()
 
 
-@pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 128), (48, 96, 640, 64), (64, 4096, 512, 32)])
-def test_gemm_tiled_on_small_m(m, n, k, g):
+@pytest.mark.parametrize("g", [32, 64, 128, 0])
+@pytest.mark.parametrize("k_split", [1, 2])
+@pytest.mark.parametrize("m", [1, 16, 33, 64])
+def test_gemm_skinny_long_wave_ranges(m, g, k_split):
+    """Each wave streams many blocks through its ring (steady state runs
+    several times), for every group size: the ring's meta reuse must hold."""
+    n, k = 96, 2688                                  # 21 k-blocks: ragged last group
+    w, a, out = _layer(m, n, k, g, "student_t4", seed=300 + m + g)
+    blob = w4.pack(w, g)
+    log(f"gemm skinny long ranges m={m} n={n} k={k} g={g} k_split={k_split}")
+    for nt in (1, 2, 4):
+        if m > 16 and nt == 4:
+            continue
+        y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=1, k_split=k_split,
+                          n_tiles=nt)
+        assert np.array_equal(acc, out["acc"]), f"n_tiles={nt}"
+        assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 128), (48, 96, 640, 64), (64, 4096, 512, 32),
+                                     (200, 272, 2688, 128), (130, 1040, 1152, 0)])
+def test_gemm_tiled_every_tile_shape(m, n, k, g):
     w, a, out = _layer(m, n, k, g, "student_t4", seed=90 + m)
     blob = w4.pack(w, g)
-    log(f"gemm tiled m={m} n={n} k={k} g={g}")
-    y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=2)
-    assert np.array_equal(acc, out["acc"])
-    assert ref.y_tolerance_ok(y, out["y"]).all()
+    for mt, nt in ((0, 0), (4, 4), (8, 4), (8, 2)):
+        log(f"gemm tiled m={m} n={n} k={k} g={g} m_tiles={mt} n_tiles={nt}")
+        y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=2, m_tiles=mt,
+                          n_tiles=nt)
+        assert np.array_equal(acc, out["acc"]), (mt, nt)
+        assert ref.y_tolerance_ok(y, out["y"]).all()
 
 
 def test_gemm_extreme_operands():

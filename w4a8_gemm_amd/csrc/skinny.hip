@@ -80,11 +80,14 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
     for (int c = 0; c < NC; ++c) acc[i][c] = v4i{0, 0, 0, 0};
 
   // Ring slot j holds block kb0 + j.  kbw is a multiple of D = 4, so slot 0
-  // always starts a meta dword; a dword covers 4 / GPB blocks, and only the
-  // slots that start one load it (g = 128: one meta load per 4 blocks).
+  // always starts a meta dword; a dword covers MSTEP = 4 / GPB blocks, and
+  // only the slots that start one load it (g = 128: one meta load per 4
+  // blocks).  Meta loads land in mdn (next group) and become md (current
+  // group) once the current group has been decoded, because the slots of a
+  // group that share a dword are decoded after slot 0 has been refilled.
   constexpr int MSTEP = GPB == 0 ? D : 4 / GPB;   // slots per meta dword
   u32x4 q[D][NC];
-  uint32_t md[D][NC];
+  uint32_t md[D][NC], mdn[D][NC];
   v4i a[D][MR][2];
   auto issue = [&](int j, int slot_kb) {
     const int kb = min(slot_kb, kb_last);
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
       q[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qptr[c] + size_t(kb) * 1024));
     if (j % MSTEP == 0) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) md[j][c] = mrow[c][GPB == 0 ? 0 : (kb * GPB) >> 2];
+      for (int c = 0; c < NC; ++c) mdn[j][c] = mrow[c][GPB == 0 ? 0 : (kb * GPB) >> 2];
     }
     // only lanes that hold a real token row fetch activations
 #pragma unroll
@@ -104,6 +107,12 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
           a[j][i][h] = *reinterpret_cast<const v4i*>(aptr[i] + kb * 128 + 64 * h);
       }
     }
+  };
+  auto next_group_meta = [&]() {
+#pragma unroll
+    for (int j = 0; j < D; j += MSTEP)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) md[j][c] = mdn[j][c];
   };
 
   // decode block kb from ring slot j and multiply it into acc
@@ -143,6 +152,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
   if (kb_begin < kb_end) {
 #pragma unroll
     for (int j = 0; j < D; ++j) issue(j, kb_begin + j);
+    next_group_meta();
     int kb0 = kb_begin;
     // steady state: D blocks in flight; every load is unconditional (clamped)
     for (; kb0 + D < kb_end; kb0 += D) {
@@ -151,6 +161,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
         compute(j, kb0 + j);
         issue(j, kb0 + D + j);
       }
+      next_group_meta();
     }
     // last group: no further loads
 #pragma unroll

@@ -1,4 +1,29 @@
 // W4A8 GEMM for gfx950 (CDNA4): the tiled kernel for larger M.
+//
+// Y[m,n] = fp16(s_a[m] * s1[n] * sum_k A8[m,k] * W8^[n,k]),  W8^ = (q - z) * s2.
+//
+// Once M reaches a few hundred tokens the layer is bound by the int8 MFMA
+// rate, and the cost that progressive quantization targets (the QServe/QoQ
+// abstract: dequantization on the slow general-purpose cores) is the decode
+// of the 4-bit codes.  The tiling keeps that decode off the critical path:
+//
+//  * A workgroup of NW = 4 waves computes a BM x BN tile, BM = 16 * MR rows
+//    and BN = NW * NC * 16 columns.  Every wave owns ALL BM rows and its own
+//    NC column tiles, so each weight code is decoded exactly once per
+//    workgroup and each decoded operand feeds MR MFMAs.
+//  * The activation tile (BM rows x 128 k) goes from HBM to LDS with
+//    direct-to-LDS 128-bit loads (no staging registers), double-buffered
+//    across k-blocks.  Its 16-byte chunks are XOR-swizzled by row so that the
+//    ds_read_b128 operand reads of 16 consecutive rows do not collide on LDS
+//    banks.
+//  * Weight codes go from HBM straight into registers (the layout already
+//    matches the MFMA B operand, so there is no LDS round trip for weights —
+//    the point of the offline interleaving in the QUICK abstract) and are
+//    prefetched one k-block ahead.
+//  * Workgroups are mapped to tiles XCD by XCD, and within an XCD in groups
+//    of GROUP_M row tiles, so that the workgroups resident on one XCD at the
+//    same time share weight columns and activation rows in that XCD's L2.
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -10,38 +35,81 @@ namespace {
 
 using namespace dev;
 
-// ---------------------------------------------------------------- tiled
-// Larger M.  Workgroup = NW waves along N; wave wn owns column tiles
-// [(bx*NW + wn)*NC, +NC) and row tiles [by*MR, +MR) over all of K, so no
-// weight is decoded twice in a workgroup.
+constexpr int kNumXcd = 8;     // MI355X: 8 accelerator complex dies, round-robin dispatch
+constexpr int kGroupM = 8;     // row tiles per raster group
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Map the linear workgroup id to (row tile, column tile): XCD-major, then
+// grouped raster inside the XCD's share.
+__device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int* bm, int* bn) {
+  const int total = nbm * nbn;
+  int logical = bid;
+  if (total % kNumXcd == 0) {
+    const int per = total / kNumXcd;
+    logical = (bid % kNumXcd) * per + bid / kNumXcd;
+  }
+  const int group_size = kGroupM * nbn;
+  const int group = logical / group_size;
+  const int first_m = group * kGroupM;
+  const int gm = min(nbm - first_m, kGroupM);
+  const int in_group = logical % group_size;
+  *bm = first_m + in_group % gm;
+  *bn = in_group / gm;
+}
+
 template <int MR, int NC, int NW, int GPB>
 __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
+  constexpr int BM = 16 * MR;
+  constexpr int A_STAGE = BM * 128;              // bytes of one activation tile
+  constexpr int CPW = BM * 8 / (64 * NW);        // 16-byte chunks per lane per tile
+  static_assert(CPW >= 1 && BM * 8 % (64 * NW) == 0, "tile must split evenly over lanes");
+  __shared__ __attribute__((aligned(16))) uint8_t As[2 * A_STAGE];
+
   const int lane = threadIdx.x & 63;
-  const int wn = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quarter = lane >> 4;
   const int r16 = lane & 15;
 
   const int ntiles = p.n >> 4;
   const int kblocks = p.k >> 7;
-  const int tile0 = (blockIdx.x * NW + wn) * NC;
-  const int row_tile0 = blockIdx.y * MR;
+  const int nbm = (p.m + BM - 1) / BM;
+  const int nbn = (ntiles + NW * NC - 1) / (NW * NC);
+  int bm, bn;
+  tile_of(blockIdx.x, nbm, nbn, &bm, &bn);
+  const int row0 = bm * BM;
+  const int tile0 = (bn * NW + wave) * NC;
 
+  // weight codes and meta of this wave's column tiles
   const uint8_t* qptr[NC];
-  const uint8_t* mrow[NC];
+  const uint32_t* mrow[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int t = min(tile0 + c, ntiles - 1);
     qptr[c] = p.q + (size_t(t) * kblocks * 64 + lane) * 16;
-    mrow[c] = p.meta + size_t(t * 16 + r16) * p.meta_row_bytes;
+    mrow[c] = reinterpret_cast<const uint32_t*>(p.meta + size_t(t * 16 + r16) * p.meta_row_bytes);
   }
-  const int8_t* aptr[MR];
+  // Activation tile loads: instruction j of this wave fills LDS slots
+  // [(wave * CPW + j) * 64, +64) of 16 bytes; slot s holds row s / 8,
+  // physical chunk s % 8, i.e. logical chunk (s % 8) ^ (row % 8).
+  const int8_t* agp[CPW];
 #pragma unroll
-  for (int i = 0; i < MR; ++i) {
-    const int row = min((row_tile0 + i) * 16 + r16, p.m - 1);
-    aptr[i] = p.a8 + size_t(row) * p.lda8 + 16 * quarter;
+  for (int j = 0; j < CPW; ++j) {
+    const int s = (wave * CPW + j) * 64 + lane;
+    const int row = s >> 3;
+    const int lchunk = (s & 7) ^ (row & 7);
+    agp[j] = p.a8 + size_t(min(row0 + row, p.m - 1)) * p.lda8 + lchunk * 16;
   }
-
-  const EpiScales<MR, NC> es = load_scales<MR, NC>(p, row_tile0, tile0, lane);
+  // operand reads: row i*16 + r16, logical chunk 4h + quarter
+  int a_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) a_off[h] = r16 * 128 + (((4 * h + quarter) ^ (r16 & 7)) * 16);
 
   v4i acc[MR][NC];
 #pragma unroll
@@ -49,68 +117,84 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[i][c] = v4i{0, 0, 0, 0};
 
-  uint4 qcur[NC];
-  uint32_t mcur[2][NC];
-  v4i acur[MR][2];
-  auto load_block = [&](int kb, uint4 (&qv)[NC], uint32_t (&mv)[2][NC], v4i (&av)[MR][2]) {
+  auto issue_a = [&](int kb, int stage) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qv[c] = *reinterpret_cast<const uint4*>(qptr[c] + size_t(kb) * 1024);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kc = 64 * h + 16 * quarter;
-        const int grp = GPB == 0 ? 0 : kb * GPB + ((kc * GPB) >> 7);
-        mv[h][c] = meta_byte(mrow[c], grp);
-      }
+    for (int j = 0; j < CPW; ++j) {
+      uint8_t* dst = As + stage * A_STAGE + (wave * CPW + j) * 1024;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(agp[j] + kb * 128),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < MR; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) av[i][h] = *reinterpret_cast<const v4i*>(aptr[i] + kb * 128 + 64 * h);
   };
-  load_block(0, qcur, mcur, acur);
-  for (int kb = 0; kb < kblocks; ++kb) {
-    uint4 qnext[NC];
-    uint32_t mnext[2][NC];
-    v4i anext[MR][2];
-    const bool more = kb + 1 < kblocks;
-    if (more) load_block(kb + 1, qnext, mnext, anext);
+  u32x4 qcur[NC], qnext[NC];
+  uint32_t mcur[NC], mnext[NC];
+  auto issue_w = [&](int kb, u32x4 (&qs)[NC], uint32_t (&ms)[NC]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qs[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qptr[c] + size_t(kb) * 1024));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ms[c] = mrow[c][GPB == 0 ? 0 : (kb * GPB) >> 2];
+  };
+
+  auto compute = [&](int kb, const uint8_t* at) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      int byte = 0;
+      if (GPB == 1) byte = kb & 3;
+      if (GPB == 2) byte = 2 * (kb & 1) + h;
+      if (GPB == 4) byte = 2 * h + (quarter >> 1);
       v4i bf[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        const GroupConst gc = group_const((mcur[c] >> (8 * byte)) & 0xFFu);
         const uint32_t w0 = h ? qcur[c].z : qcur[c].x;
         const uint32_t w1 = h ? qcur[c].w : qcur[c].y;
-        bf[c] = decode16(w0, w1, group_const(mcur[h][c]));
-      }
-#pragma unroll
-      for (int i = 0; i < MR; ++i)
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          acc[i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(acur[i][h], bf[c], acc[i][c], 0, 0, 0);
-    }
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qcur[c] = qnext[c];
-        mcur[0][c] = mnext[0][c];
-        mcur[1][c] = mnext[1][c];
+        bf[c] = decode16(w0, w1, gc);
       }
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        acur[i][0] = anext[i][0];
-        acur[i][1] = anext[i][1];
+        const v4i af = *reinterpret_cast<const v4i*>(at + i * 16 * 128 + a_off[h]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc[i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c], acc[i][c], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: while block kb is multiplied, the activation tile of kb + 1 is
+  // landing in the other LDS stage and the weight codes of kb + 1 in the
+  // other registers.  Loads per lane per block: CPW (to LDS) + 2 * NC.  The
+  // last iteration re-loads the last block (clamped) so that the loop body
+  // has no branch; that copy is never read.
+  issue_a(0, 0);
+  issue_w(0, qcur, mcur);
+  for (int kb = 0; kb < kblocks; ++kb) {
+    const int stage = kb & 1;
+    const int nxt = min(kb + 1, kblocks - 1);
+    issue_a(nxt, stage ^ 1);
+    issue_w(nxt, qnext, mnext);
+    wait_vm<CPW + 2 * NC>();       // block kb's loads (issued one iteration ago) are done
+    __builtin_amdgcn_s_barrier();  // every wave's share of tile kb is in LDS
+    compute(kb, As + stage * A_STAGE);
+    __builtin_amdgcn_s_barrier();  // stage is free for block kb + 2
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qcur[c] = qnext[c];
+      mcur[c] = mnext[c];
+    }
   }
+  wait_vm<0>();                    // no LDS write still in flight at exit
+
+  // scales are fetched only now: this kernel runs long enough that one
+  // more round trip at the end does not matter, and keeping them live
+  // through the K loop would cost registers
+  const EpiScales<MR, NC> es = load_scales<MR, NC>(p, row0 / 16, tile0, lane);
 #pragma unroll
   for (int i = 0; i < MR; ++i)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (tile0 + c >= ntiles) continue;
       int32_t v[4] = {acc[i][c][0], acc[i][c][1], acc[i][c][2], acc[i][c][3]};
-      store_frag(p, (row_tile0 + i) * 16, (tile0 + c) * 16, lane, v, es.s1[c], es.sa[i]);
+      store_frag(p, row0 + i * 16, (tile0 + c) * 16, lane, v, es.s1[c], es.sa[i]);
     }
 }
 
@@ -118,7 +202,9 @@ template <int MR, int NC, int GPB>
 hipError_t launch_tiled_t(const GemmParams& p, hipStream_t stream) {
   constexpr int NW = 4;
   const int ntiles = p.n / 16;
-  dim3 grid((ntiles + NW * NC - 1) / (NW * NC), (p.m + 16 * MR - 1) / (16 * MR));
+  const int nbm = (p.m + 16 * MR - 1) / (16 * MR);
+  const int nbn = (ntiles + NW * NC - 1) / (NW * NC);
+  dim3 grid(nbm * nbn);
   dim3 block(64 * NW);
   GemmParams arg = p;
   void* args[] = {&arg};
@@ -140,13 +226,16 @@ hipError_t tiled_by_gpb(const GemmParams& p, int gpb, hipStream_t s) {
 }  // namespace
 
 bool tiled_config_supported(const TiledConfig& c) {
-  return c.mr == 4 && (c.nc == 4 || c.nc == 2) && c.nw == 4;
+  return c.nw == 4 && ((c.mr == 8 && c.nc == 4) || (c.mr == 4 && c.nc == 4) ||
+                       (c.mr == 8 && c.nc == 2));
 }
 
 hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
                              hipStream_t stream) {
-  if (c.mr == 4 && c.nc == 4 && c.nw == 4) return tiled_by_gpb<4, 4>(p, gpb, stream);
-  if (c.mr == 4 && c.nc == 2 && c.nw == 4) return tiled_by_gpb<4, 2>(p, gpb, stream);
+  if (c.nw != 4) return hipErrorInvalidValue;
+  if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4>(p, gpb, stream);
+  if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4>(p, gpb, stream);
+  if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2>(p, gpb, stream);
   return hipErrorInvalidValue;
 }
 
