@@ -142,7 +142,8 @@ typedef struct {
   int k_split;   /* skinny: waves that share one K range (1..8), 0 = auto */
   int n_tiles;   /* 16-column tiles per wave: skinny 1, 2 or 4; tiled 2 or 4; 0 = auto */
   int m_tiles;   /* tiled: 16-row tiles per workgroup (4 or 8), 0 = auto */
-  int reserved[4];
+  int stages;    /* tiled: LDS pipeline stages (2 or 3), 0 = auto */
+  int reserved[3];
 } w4a8_gemm_opts;
 
 size_t w4a8_gemm_workspace_size(int m, int n, int k, int g);

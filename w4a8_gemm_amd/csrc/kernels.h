@@ -37,9 +37,10 @@ struct SkinnyConfig {
 };
 
 struct TiledConfig {
-  int mr;   // 16-row tiles per wave
-  int nc;   // 16-column tiles per wave
-  int nw;   // waves along N per workgroup
+  int mr;       // 16-row tiles per wave
+  int nc;       // 16-column tiles per wave
+  int nw;       // waves along N per workgroup
+  int stages;   // LDS pipeline stages (2 or 3; 0 = default 2)
 };
 
 hipError_t launch_quant_act(const uint16_t* a, int m, int k, int lda, int8_t* a8, int lda8,

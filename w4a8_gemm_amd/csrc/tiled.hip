@@ -64,13 +64,18 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int* bm, int*
   *bn = in_group / gm;
 }
 
-template <int MR, int NC, int NW, int GPB>
-__global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
+template <int MR, int NC, int NW, int GPB, int S>
+__global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
   constexpr int BM = 16 * MR;
-  constexpr int A_STAGE = BM * 128;              // bytes of one activation tile
-  constexpr int CPW = BM * 8 / (64 * NW);        // 16-byte chunks per lane per tile
+  constexpr int A_BYTES = BM * 128;              // activation tile of one k-block
+  constexpr int W_BYTES = NW * NC * 1024;        // weight codes of one k-block
+  constexpr int M_BYTES = NW * NC * 256;         // meta dwords of one k-block
+  constexpr int STAGE = A_BYTES + W_BYTES + M_BYTES;
+  constexpr int CPW = BM * 8 / (64 * NW);        // activation chunks per lane
+  constexpr int LOADS = CPW + 2 * NC;            // vector-memory ops per lane per k-block
   static_assert(CPW >= 1 && BM * 8 % (64 * NW) == 0, "tile must split evenly over lanes");
-  __shared__ __attribute__((aligned(16))) uint8_t As[2 * A_STAGE];
+  static_assert(S >= 2 && (S - 2) * LOADS < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // S stages
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -86,7 +91,6 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
   const int row0 = bm * BM;
   const int tile0 = (bn * NW + wave) * NC;
 
-  // weight codes and meta of this wave's column tiles
   const uint8_t* qptr[NC];
   const uint32_t* mrow[NC];
 #pragma unroll
@@ -95,9 +99,9 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
     qptr[c] = p.q + (size_t(t) * kblocks * 64 + lane) * 16;
     mrow[c] = reinterpret_cast<const uint32_t*>(p.meta + size_t(t * 16 + r16) * p.meta_row_bytes);
   }
-  // Activation tile loads: instruction j of this wave fills LDS slots
-  // [(wave * CPW + j) * 64, +64) of 16 bytes; slot s holds row s / 8,
-  // physical chunk s % 8, i.e. logical chunk (s % 8) ^ (row % 8).
+  // Activation tile: instruction j of this wave fills 16-byte slots
+  // [(wave * CPW + j) * 64, +64); slot s holds row s / 8, physical chunk
+  // s % 8, i.e. logical chunk (s % 8) ^ (row % 8).
   const int8_t* agp[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
@@ -110,6 +114,9 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
   int a_off[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) a_off[h] = r16 * 128 + (((4 * h + quarter) ^ (r16 & 7)) * 16);
+  // this wave's weight codes and meta inside a stage (lane-linear, as loaded)
+  const int w_off = A_BYTES + wave * NC * 1024 + lane * 16;
+  const int m_off = A_BYTES + W_BYTES + wave * NC * 256 + lane * 4;
 
   v4i acc[MR][NC];
 #pragma unroll
@@ -117,25 +124,32 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[i][c] = v4i{0, 0, 0, 0};
 
-  auto issue_a = [&](int kb, int stage) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  // every load of k-block kb goes straight to LDS stage `stage`
+  auto issue = [&](int kb, int stage) {
+    uint8_t* st = smem + stage * STAGE;
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      uint8_t* dst = As + stage * A_STAGE + (wave * CPW + j) * 1024;
+    for (int j = 0; j < CPW; ++j)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(agp[j] + kb * 128),
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-    }
-  };
-  u32x4 qcur[NC], qnext[NC];
-  uint32_t mcur[NC], mnext[NC];
-  auto issue_w = [&](int kb, u32x4 (&qs)[NC], uint32_t (&ms)[NC]) {
+                                       (lds_ptr)(st + (wave * CPW + j) * 1024), 16, 0, 0);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qs[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qptr[c] + size_t(kb) * 1024));
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(qptr[c] + size_t(kb) * 1024),
+                                       (lds_ptr)(st + A_BYTES + (wave * NC + c) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) ms[c] = mrow[c][GPB == 0 ? 0 : (kb * GPB) >> 2];
+    for (int c = 0; c < NC; ++c)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(mrow[c] + (GPB == 0 ? 0 : (kb * GPB) >> 2)),
+                                       (lds_ptr)(st + A_BYTES + W_BYTES + (wave * NC + c) * 256), 4, 0, 0);
   };
 
-  auto compute = [&](int kb, const uint8_t* at) {
+  auto compute = [&](int kb, const uint8_t* st) {
+    u32x4 qv[NC];
+    uint32_t mv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qv[c] = *reinterpret_cast<const u32x4*>(st + w_off + c * 1024);
+      mv[c] = *reinterpret_cast<const uint32_t*>(st + m_off + c * 256);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       int byte = 0;
@@ -145,14 +159,14 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
       v4i bf[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const GroupConst gc = group_const((mcur[c] >> (8 * byte)) & 0xFFu);
-        const uint32_t w0 = h ? qcur[c].z : qcur[c].x;
-        const uint32_t w1 = h ? qcur[c].w : qcur[c].y;
+        const GroupConst gc = group_const((mv[c] >> (8 * byte)) & 0xFFu);
+        const uint32_t w0 = h ? qv[c].z : qv[c].x;
+        const uint32_t w1 = h ? qv[c].w : qv[c].y;
         bf[c] = decode16(w0, w1, gc);
       }
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        const v4i af = *reinterpret_cast<const v4i*>(at + i * 16 * 128 + a_off[h]);
+        const v4i af = *reinterpret_cast<const v4i*>(st + i * 16 * 128 + a_off[h]);
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           acc[i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[c], acc[i][c], 0, 0, 0);
@@ -160,27 +174,18 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
     }
   };
 
-  // Pipeline: while block kb is multiplied, the activation tile of kb + 1 is
-  // landing in the other LDS stage and the weight codes of kb + 1 in the
-  // other registers.  Loads per lane per block: CPW (to LDS) + 2 * NC.  The
-  // last iteration re-loads the last block (clamped) so that the loop body
-  // has no branch; that copy is never read.
-  issue_a(0, 0);
-  issue_w(0, qcur, mcur);
-  for (int kb = 0; kb < kblocks; ++kb) {
-    const int stage = kb & 1;
-    const int nxt = min(kb + 1, kblocks - 1);
-    issue_a(nxt, stage ^ 1);
-    issue_w(nxt, qnext, mnext);
-    wait_vm<CPW + 2 * NC>();       // block kb's loads (issued one iteration ago) are done
-    __builtin_amdgcn_s_barrier();  // every wave's share of tile kb is in LDS
-    compute(kb, As + stage * A_STAGE);
-    __builtin_amdgcn_s_barrier();  // stage is free for block kb + 2
+  // Pipeline of depth S - 1: at iteration kb the loads of k-blocks
+  // kb + 1 .. kb + S - 2 are in flight; block kb + S - 1 is issued into the
+  // stage that iteration kb - 1 consumed, after the barrier that proves
+  // every wave is done with it.  Loads past the end re-read the last block
+  // into a stage that is never read again, so the loop has no branch.
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qcur[c] = qnext[c];
-      mcur[c] = mnext[c];
-    }
+  for (int j = 0; j < S - 1; ++j) issue(min(j, kblocks - 1), j);
+  for (int kb = 0; kb < kblocks; ++kb) {
+    wait_vm<(S - 2) * LOADS>();    // this wave's loads of block kb have landed
+    __builtin_amdgcn_s_barrier();  // ... and every other wave's share of the tile
+    issue(min(kb + S - 1, kblocks - 1), (kb + S - 1) % S);
+    compute(kb, smem + (kb % S) * STAGE);
   }
   wait_vm<0>();                    // no LDS write still in flight at exit
 
@@ -198,9 +203,18 @@ __global__ __launch_bounds__(64 * NW) void tiled_kernel(GemmParams p) {
     }
 }
 
-template <int MR, int NC, int GPB>
+template <int MR, int NC, int GPB, int S>
 hipError_t launch_tiled_t(const GemmParams& p, hipStream_t stream) {
   constexpr int NW = 4;
+  constexpr int STAGE = 16 * MR * 128 + NW * NC * (1024 + 256);
+  const void* fn = reinterpret_cast<const void*>(&tiled_kernel<MR, NC, NW, GPB, S>);
+  const size_t lds = size_t(S) * STAGE;
+  if (lds > 65536) {
+    // above the default dynamic-LDS limit: opt in once (the attribute is
+    // per kernel and process-wide, setting it again is harmless)
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
   const int ntiles = p.n / 16;
   const int nbm = (p.m + 16 * MR - 1) / (16 * MR);
   const int nbn = (ntiles + NW * NC - 1) / (NW * NC);
@@ -208,17 +222,16 @@ hipError_t launch_tiled_t(const GemmParams& p, hipStream_t stream) {
   dim3 block(64 * NW);
   GemmParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&tiled_kernel<MR, NC, NW, GPB>), grid,
-                         block, args, 0, stream);
+  return hipLaunchKernel(fn, grid, block, args, lds, stream);
 }
 
-template <int MR, int NC>
+template <int MR, int NC, int S>
 hipError_t tiled_by_gpb(const GemmParams& p, int gpb, hipStream_t s) {
   switch (gpb) {
-    case 0: return launch_tiled_t<MR, NC, 0>(p, s);
-    case 1: return launch_tiled_t<MR, NC, 1>(p, s);
-    case 2: return launch_tiled_t<MR, NC, 2>(p, s);
-    case 4: return launch_tiled_t<MR, NC, 4>(p, s);
+    case 0: return launch_tiled_t<MR, NC, 0, S>(p, s);
+    case 1: return launch_tiled_t<MR, NC, 1, S>(p, s);
+    case 2: return launch_tiled_t<MR, NC, 2, S>(p, s);
+    case 4: return launch_tiled_t<MR, NC, 4, S>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -226,16 +239,23 @@ hipError_t tiled_by_gpb(const GemmParams& p, int gpb, hipStream_t s) {
 }  // namespace
 
 bool tiled_config_supported(const TiledConfig& c) {
-  return c.nw == 4 && ((c.mr == 8 && c.nc == 4) || (c.mr == 4 && c.nc == 4) ||
-                       (c.mr == 8 && c.nc == 2));
+  const bool stages_ok = c.stages == 0 || c.stages == 2 || c.stages == 3;
+  return c.nw == 4 && stages_ok &&
+         ((c.mr == 8 && c.nc == 4) || (c.mr == 4 && c.nc == 4) || (c.mr == 8 && c.nc == 2));
 }
 
 hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
                              hipStream_t stream) {
   if (c.nw != 4) return hipErrorInvalidValue;
-  if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4>(p, gpb, stream);
-  if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4>(p, gpb, stream);
-  if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2>(p, gpb, stream);
+  if (c.stages == 3) {
+    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 3>(p, gpb, stream);
+    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 3>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 3>(p, gpb, stream);
+  } else {
+    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 2>(p, gpb, stream);
+    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 2>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 2>(p, gpb, stream);
+  }
   return hipErrorInvalidValue;
 }
 
