@@ -145,16 +145,16 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
     e = launch_gemm_skinny(p, gpb, c, s);
   } else {
     // Tiled: 128 x 256 tiles with a 2-stage pipeline (two workgroups per
-    // compute unit) once there are enough tiles to give every compute unit
-    // work; otherwise 64 x 256 tiles with 3 stages (rocprofv3 sweeps).
+    // compute unit) once there are enough tiles to keep most compute units
+    // busy; otherwise 64 x 256 tiles with 3 stages (rocprofv3 sweeps).
     TiledConfig c;
     c.nw = 4;
     c.nc = 4;
     const long tiles128 = long((m + 127) / 128) * long((n / kColTile + 15) / 16);
-    c.mr = tiles128 >= 256 ? 8 : 4;
+    c.mr = tiles128 >= 192 ? 8 : 4;
+    if (opts && opts->m_tiles > 0) c.mr = opts->m_tiles;
     c.stages = c.mr == 8 ? 2 : 3;
     if (opts && opts->stages > 0) c.stages = opts->stages;
-    if (opts && opts->m_tiles > 0) c.mr = opts->m_tiles;
     if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
     if (!tiled_config_supported(c)) return W4A8_ERR_INVALID_ARGUMENT;
     e = launch_gemm_tiled(p, gpb, c, s);

@@ -38,6 +38,25 @@ using namespace dev;
 constexpr int kNumXcd = 8;     // MI355X: 8 accelerator complex dies, round-robin dispatch
 constexpr int kGroupM = 8;     // row tiles per raster group
 
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor, 32-bit
+// data format; out-of-range reads return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Buffer loads that write straight to LDS: lane i's `size` bytes from
+// base + voffset + soffset land at dst + i * size.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voffset,
+                                                uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voffset,
+                                               uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 4, voffset, soffset, 0, 0);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14).
 template <int N>
@@ -91,24 +110,37 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
   const int row0 = bm * BM;
   const int tile0 = (bn * NW + wave) * NC;
 
-  const uint8_t* qptr[NC];
-  const uint32_t* mrow[NC];
+  // Loads go through buffer resources: the base is wave-uniform (scalar
+  // registers), each lane adds one fixed 32-bit offset and each k-block one
+  // scalar offset, so issuing a load costs no vector arithmetic.  Offsets
+  // past a resource's size would read 0; every offset below is in range.
+  const int tlo = min(tile0, ntiles - 1);
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(
+      p.q + size_t(tlo) * kblocks * 1024, uint32_t(NC) * uint32_t(kblocks) * 1024u);
+  const __amdgpu_buffer_rsrc_t m_rsrc = make_rsrc(
+      p.meta + size_t(tlo) * 16 * p.meta_row_bytes, uint32_t(NC) * 16u * uint32_t(p.meta_row_bytes));
+  const uint32_t q_lane = uint32_t(lane) * 16;
+  const uint32_t m_lane = uint32_t(r16) * uint32_t(p.meta_row_bytes);
+  uint32_t q_tile[NC], m_tile[NC];                              // clamped column tiles
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int t = min(tile0 + c, ntiles - 1);
-    qptr[c] = p.q + (size_t(t) * kblocks * 64 + lane) * 16;
-    mrow[c] = reinterpret_cast<const uint32_t*>(p.meta + size_t(t * 16 + r16) * p.meta_row_bytes);
+    const int t = min(tile0 + c, ntiles - 1) - tlo;
+    q_tile[c] = uint32_t(t) * uint32_t(kblocks) * 1024u;
+    m_tile[c] = uint32_t(t) * 16u * uint32_t(p.meta_row_bytes);
   }
   // Activation tile: instruction j of this wave fills 16-byte slots
   // [(wave * CPW + j) * 64, +64); slot s holds row s / 8, physical chunk
-  // s % 8, i.e. logical chunk (s % 8) ^ (row % 8).
-  const int8_t* agp[CPW];
+  // s % 8, i.e. logical chunk (s % 8) ^ (row % 8).  Offsets are relative to
+  // row0 (rows past M read row M - 1, whose results are never stored).
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      make_rsrc(p.a8 + size_t(row0) * p.lda8, uint32_t(BM) * uint32_t(p.lda8));
+  uint32_t a_lane[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int s = (wave * CPW + j) * 64 + lane;
     const int row = s >> 3;
     const int lchunk = (s & 7) ^ (row & 7);
-    agp[j] = p.a8 + size_t(min(row0 + row, p.m - 1)) * p.lda8 + lchunk * 16;
+    a_lane[j] = uint32_t(min(row0 + row, p.m - 1) - row0) * uint32_t(p.lda8) + uint32_t(lchunk * 16);
   }
   // operand reads: row i*16 + r16, logical chunk 4h + quarter
   int a_off[2];
@@ -124,22 +156,20 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[i][c] = v4i{0, 0, 0, 0};
 
-  typedef __attribute__((address_space(3))) void* lds_ptr;
   // every load of k-block kb goes straight to LDS stage `stage`
   auto issue = [&](int kb, int stage) {
     uint8_t* st = smem + stage * STAGE;
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(agp[j] + kb * 128),
-                                       (lds_ptr)(st + (wave * CPW + j) * 1024), 16, 0, 0);
+      buffer_to_lds16(a_rsrc, st + (wave * CPW + j) * 1024, a_lane[j], uint32_t(kb) * 128u);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(qptr[c] + size_t(kb) * 1024),
-                                       (lds_ptr)(st + A_BYTES + (wave * NC + c) * 1024), 16, 0, 0);
+      buffer_to_lds16(q_rsrc, st + A_BYTES + (wave * NC + c) * 1024, q_lane,
+                      q_tile[c] + uint32_t(kb) * 1024u);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(mrow[c] + (GPB == 0 ? 0 : (kb * GPB) >> 2)),
-                                       (lds_ptr)(st + A_BYTES + W_BYTES + (wave * NC + c) * 256), 4, 0, 0);
+      buffer_to_lds4(m_rsrc, st + A_BYTES + W_BYTES + (wave * NC + c) * 256, m_lane,
+                     m_tile[c] + (GPB == 0 ? 0u : uint32_t((kb * GPB) >> 2) * 4u));
   };
 
   auto compute = [&](int kb, const uint8_t* st) {
@@ -150,16 +180,22 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
       qv[c] = *reinterpret_cast<const u32x4*>(st + w_off + c * 1024);
       mv[c] = *reinterpret_cast<const uint32_t*>(st + m_off + c * 256);
     }
+    // g >= 128 or per channel: both halves of the block share one group
+    GroupConst gblk[NC];
+    if (GPB <= 1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        gblk[c] = group_const((mv[c] >> (GPB == 1 ? 8 * (kb & 3) : 0)) & 0xFFu);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       int byte = 0;
-      if (GPB == 1) byte = kb & 3;
       if (GPB == 2) byte = 2 * (kb & 1) + h;
       if (GPB == 4) byte = 2 * h + (quarter >> 1);
       v4i bf[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const GroupConst gc = group_const((mv[c] >> (8 * byte)) & 0xFFu);
+        const GroupConst gc = GPB <= 1 ? gblk[c] : group_const((mv[c] >> (8 * byte)) & 0xFFu);
         const uint32_t w0 = h ? qv[c].z : qv[c].x;
         const uint32_t w1 = h ? qv[c].w : qv[c].y;
         bf[c] = decode16(w0, w1, gc);
