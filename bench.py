@@ -29,9 +29,8 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
-# counters are keyed to the kernels they were taken on
-GEMM_SRCS = [os.path.join(ROOT, "w4a8_gemm_amd", "csrc", f)
-             for f in ("skinny.hip", "gemm_common.h")]
+# HBM counters are keyed to the sources of the kernel they were taken on
+CSRC = os.path.join(ROOT, "w4a8_gemm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
@@ -49,25 +48,26 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def gemm_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for path in GEMM_SRCS:
-        with open(path, "rb") as f:
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+def load_traffic(workload):
+    """Mean HBM bytes per GEMM launch on `workload` from committed rocprofv3
+    counter runs, if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            entries = json.load(f)["entries"]
+    except (OSError, ValueError, KeyError):
         return None
-    if t.get("gemm_source_sha256_16") != gemm_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+    for t in entries:
+        if t.get("workload") == workload and t.get("source_sha256_16") == source_hash(t["sources"]):
+            return t.get("bytes_per_launch")
+    return None
 
 
 class HipEvent:
@@ -163,7 +163,13 @@ def main():
     ap.add_argument("--runs-json", default="")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step (reported as context)")
+    ap.add_argument("--print-source-hash", action="store_true",
+                    help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
+    if args.print_source_hash:
+        for files in (["skinny.hip", "gemm_common.h"], ["tiled.hip", "gemm_common.h"]):
+            print(" + ".join(files), source_hash(files))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this W4A8 GEMM build has no multi-GPU path "
@@ -316,7 +322,7 @@ def main():
     else:
         achieved = float(gemm_ops.mean()) / avg_dur / 1e12
         peak, unit, bound = INT8_PEAK_TOPS, "TFLOP/s", "mfma"
-    traffic = load_traffic() if args.workload == "llama3_8b_decode" else None
+    traffic = load_traffic(args.workload)
     value_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     value_tops = step_ops / (ms_per_step * 1e-3) / 1e12
     if hbm_bound:
