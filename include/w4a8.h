@@ -141,9 +141,12 @@ typedef struct {
   int variant;   /* 0 auto, 1 skinny (intra-workgroup split-K), 2 tiled */
   int k_split;   /* skinny: waves that share one K range (1..8), 0 = auto */
   int n_tiles;   /* 16-column tiles per wave: skinny 1, 2 or 4; tiled 2 or 4; 0 = auto */
-  int m_tiles;   /* tiled: 16-row tiles per workgroup (4 or 8), 0 = auto */
+  int m_tiles;   /* tiled: 16-row tiles per wave (4 or 8), 0 = auto */
   int stages;    /* tiled: LDS pipeline stages (2 or 3), 0 = auto */
-  int reserved[3];
+  int row_groups;/* tiled: waves along M per workgroup: 1 (4 waves) or 2
+                    (8 waves, 256 x 256 tiles, m_tiles 8 and 3 stages only),
+                    0 = auto */
+  int reserved[2];
 } w4a8_gemm_opts;
 
 size_t w4a8_gemm_workspace_size(int m, int n, int k, int g);

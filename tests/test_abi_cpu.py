@@ -208,3 +208,9 @@ def test_gpu_entry_points_validate_before_any_hip_call():
     assert call(opts=ctypes.byref(opts)) == 1
     opts = w4.GemmOpts(1, 0)
     assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 2   # skinny is M <= 64
+    # tiled shapes that do not exist: 8-wave tiles only as 8 x 4 tiles per
+    # wave with 3 stages; row groups 1 or 2; stages 2 or 3
+    for v, ks, nt, mt, st, rg in ((2, 0, 0, 4, 0, 2), (2, 0, 0, 8, 2, 2), (2, 0, 2, 8, 3, 2),
+                                  (2, 0, 0, 0, 0, 3), (2, 0, 0, 8, 4, 1), (2, 0, 0, 6, 0, 1)):
+        opts = w4.GemmOpts(v, ks, nt, mt, st, rg)
+        assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 1, (mt, st, rg)

@@ -136,15 +136,20 @@ def test_gemm_skinny_long_wave_ranges(m, g, k_split):
 
 
 @pytest.mark.parametrize("m,n,k,g", [(1, 64, 256, 128), (48, 96, 640, 64), (64, 4096, 512, 32),
-                                     (200, 272, 2688, 128), (130, 1040, 1152, 0)])
+                                     (200, 272, 2688, 128), (130, 1040, 1152, 0),
+                                     (300, 528, 1408, 64), (513, 4112, 640, 128)])
 def test_gemm_tiled_every_tile_shape(m, n, k, g):
+    """Every tiled kernel shape (row tiles per wave, column tiles per wave,
+    row groups per workgroup, stages) on ragged M and N edges."""
     w, a, out = _layer(m, n, k, g, "student_t4", seed=90 + m)
     blob = w4.pack(w, g)
-    for mt, nt in ((0, 0), (4, 4), (8, 4), (8, 2)):
-        log(f"gemm tiled m={m} n={n} k={k} g={g} m_tiles={mt} n_tiles={nt}")
+    for mt, nt, rg, st in ((0, 0, 0, 0), (4, 4, 1, 2), (4, 4, 1, 3), (8, 4, 1, 2), (8, 4, 1, 3),
+                           (8, 2, 1, 3), (8, 4, 2, 0)):
+        log(f"gemm tiled m={m} n={n} k={k} g={g} m_tiles={mt} n_tiles={nt} row_groups={rg} "
+            f"stages={st}")
         y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=2, m_tiles=mt,
-                          n_tiles=nt)
-        assert np.array_equal(acc, out["acc"]), (mt, nt)
+                          n_tiles=nt, row_groups=rg, stages=st)
+        assert np.array_equal(acc, out["acc"]), (mt, nt, rg, st)
         assert ref.y_tolerance_ok(y, out["y"]).all()
 
 

@@ -48,7 +48,8 @@ class W4A8Error(RuntimeError):
 class GemmOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("k_split", ctypes.c_int),
                 ("n_tiles", ctypes.c_int), ("m_tiles", ctypes.c_int),
-                ("stages", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
+                ("stages", ctypes.c_int), ("row_groups", ctypes.c_int),
+                ("reserved", ctypes.c_int * 2)]
 
 
 def _load():
@@ -173,7 +174,7 @@ def quant_act(a, a8=None, s_a=None, stream=None):
 
 def gemm(a8, s_a, blob_dev, n: int, k: int, g: int, y=None, acc=None, want_acc=False,
          variant: int = 0, k_split: int = 0, n_tiles: int = 0, m_tiles: int = 0,
-         stages: int = 0, workspace=None, stream=None):
+         stages: int = 0, row_groups: int = 0, workspace=None, stream=None):
     """Y = fp16(s_a * s1 * (A8 @ W8^.T)); returns y (and the int32 acc if asked)."""
     torch = _torch()
     m = a8.shape[0]
@@ -183,8 +184,8 @@ def gemm(a8, s_a, blob_dev, n: int, k: int, g: int, y=None, acc=None, want_acc=F
     if want_acc and acc is None:
         acc = torch.empty((m, n), dtype=torch.int32, device=a8.device)
     opts = None
-    if variant or k_split or n_tiles or m_tiles or stages:
-        opts = GemmOpts(variant, k_split, n_tiles, m_tiles, stages)
+    if variant or k_split or n_tiles or m_tiles or stages or row_groups:
+        opts = GemmOpts(variant, k_split, n_tiles, m_tiles, stages, row_groups)
     ws_need = int(lib.w4a8_gemm_workspace_size(m, n, k, g))
     if ws_need and workspace is None:
         workspace = torch.zeros(ws_need, dtype=torch.uint8, device=a8.device)

@@ -144,16 +144,25 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
     if (!skinny_config_supported(c, k, gpb)) return W4A8_ERR_INVALID_ARGUMENT;
     e = launch_gemm_skinny(p, gpb, c, s);
   } else {
-    // Tiled: 128 x 256 tiles with a 2-stage pipeline (two workgroups per
-    // compute unit) once there are enough tiles to keep most compute units
-    // busy; otherwise 64 x 256 tiles with 3 stages (rocprofv3 sweeps).
+    // Tiled (choices from timing sweeps on the layer shapes): 256 x 256
+    // tiles of eight waves with 3 stages when they fill every compute unit
+    // at least once; else 128 x 256 tiles of four waves with 2 stages (two
+    // workgroups per compute unit) when there are enough of them; else
+    // 64 x 256 tiles with 3 stages.
     TiledConfig c;
     c.nw = 4;
     c.nc = 4;
-    const long tiles128 = long((m + 127) / 128) * long((n / kColTile + 15) / 16);
-    c.mr = tiles128 >= 192 ? 8 : 4;
+    const long col256 = long((n / kColTile + 15) / 16);
+    const long tiles256 = long((m + 255) / 256) * col256;
+    const long tiles128 = long((m + 127) / 128) * col256;
+    c.rw = tiles256 >= 256 ? 2 : 1;
+    // a forced row-tile count or stage count without a forced row-group
+    // count selects among the four-wave kernels
+    if (opts && (opts->m_tiles > 0 || opts->stages > 0)) c.rw = 1;
+    if (opts && opts->row_groups > 0) c.rw = opts->row_groups;
+    c.mr = (c.rw == 2 || tiles128 >= 192) ? 8 : 4;
     if (opts && opts->m_tiles > 0) c.mr = opts->m_tiles;
-    c.stages = c.mr == 8 ? 2 : 3;
+    c.stages = (c.rw == 2 || c.mr == 4) ? 3 : 2;
     if (opts && opts->stages > 0) c.stages = opts->stages;
     if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
     if (!tiled_config_supported(c)) return W4A8_ERR_INVALID_ARGUMENT;

@@ -39,8 +39,9 @@ struct SkinnyConfig {
 struct TiledConfig {
   int mr;       // 16-row tiles per wave
   int nc;       // 16-column tiles per wave
-  int nw;       // waves along N per workgroup
-  int stages;   // LDS pipeline stages (2 or 3; 0 = default 2)
+  int nw;       // waves along N per workgroup (4)
+  int rw;       // waves along M per workgroup (1, or 2 for 256 x 256 tiles)
+  int stages;   // LDS pipeline stages (2 or 3)
 };
 
 hipError_t launch_quant_act(const uint16_t* a, int m, int k, int lda, int8_t* a8, int lda8,

@@ -5,21 +5,23 @@
 // Once M reaches a few hundred tokens the layer is bound by the int8 MFMA
 // rate, and the cost that progressive quantization targets (the QServe/QoQ
 // abstract: dequantization on the slow general-purpose cores) is the decode
-// of the 4-bit codes.  The tiling keeps that decode off the critical path:
+// of the 4-bit codes.  The tiling keeps that decode cheap:
 //
-//  * A workgroup of NW = 4 waves computes a BM x BN tile, BM = 16 * MR rows
-//    and BN = NW * NC * 16 columns.  Every wave owns ALL BM rows and its own
-//    NC column tiles, so each weight code is decoded exactly once per
-//    workgroup and each decoded operand feeds MR MFMAs.
-//  * The activation tile (BM rows x 128 k) goes from HBM to LDS with
-//    direct-to-LDS 128-bit loads (no staging registers), double-buffered
-//    across k-blocks.  Its 16-byte chunks are XOR-swizzled by row so that the
-//    ds_read_b128 operand reads of 16 consecutive rows do not collide on LDS
-//    banks.
-//  * Weight codes go from HBM straight into registers (the layout already
-//    matches the MFMA B operand, so there is no LDS round trip for weights —
-//    the point of the offline interleaving in the QUICK abstract) and are
-//    prefetched one k-block ahead.
+//  * A workgroup of RW x 4 waves computes a BM x BN tile, BM = RW * 16 * MR
+//    rows and BN = 4 * NC * 16 columns.  Wave (rg, cg) owns the MR row tiles
+//    of row group rg and the NC column tiles of column group cg, so each
+//    weight code is decoded RW times per workgroup and each decoded operand
+//    feeds MR MFMAs.  RW = 2 (eight waves, 256 x 256 tiles, one workgroup per
+//    compute unit) moves 28 % fewer bytes per MFMA through the vector memory
+//    path than two RW = 1 workgroups of 128 x 256.
+//  * Everything a k-block needs (the activation tile, the weight codes and
+//    their group meta) goes from HBM to LDS with direct-to-LDS 128-bit buffer
+//    loads, S stages deep, with one barrier per k-block.  The weight codes
+//    already sit in the MFMA B-operand order (the offline interleaving of the
+//    QUICK abstract), so a wave reads its codes with one ds_read_b128 per
+//    column tile.  The activation tile's 16-byte chunks are XOR-swizzled by
+//    row so that the ds_read_b128 operand reads of 16 consecutive rows do not
+//    collide on LDS banks.
 //  * Workgroups are mapped to tiles XCD by XCD, and within an XCD in groups
 //    of GROUP_M row tiles, so that the workgroups resident on one XCD at the
 //    same time share weight columns and activation rows in that XCD's L2.
@@ -83,21 +85,35 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int* bm, int*
   *bn = in_group / gm;
 }
 
-template <int MR, int NC, int NW, int GPB, int S>
-__global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
-  constexpr int BM = 16 * MR;
+constexpr int kColGroups = 4;   // waves along N per workgroup
+
+template <int MR, int NC, int RW>
+constexpr int tiled_stage_bytes() {
+  return RW * 16 * MR * 128 + kColGroups * NC * (1024 + 256);
+}
+
+template <int MR, int NC, int RW, int GPB, int S>
+__global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(GemmParams p) {
+  constexpr int NW = kColGroups;
+  constexpr int WAVES = NW * RW;
+  constexpr int BM = RW * 16 * MR;
   constexpr int A_BYTES = BM * 128;              // activation tile of one k-block
   constexpr int W_BYTES = NW * NC * 1024;        // weight codes of one k-block
   constexpr int M_BYTES = NW * NC * 256;         // meta dwords of one k-block
   constexpr int STAGE = A_BYTES + W_BYTES + M_BYTES;
-  constexpr int CPW = BM * 8 / (64 * NW);        // activation chunks per lane
-  constexpr int LOADS = CPW + 2 * NC;            // vector-memory ops per lane per k-block
-  static_assert(CPW >= 1 && BM * 8 % (64 * NW) == 0, "tile must split evenly over lanes");
+  static_assert(STAGE == tiled_stage_bytes<MR, NC, RW>(), "stage layout");
+  constexpr int CPW = BM * 8 / (64 * WAVES);     // activation chunks per lane
+  constexpr int NCL = NC / RW;                   // column tiles whose codes this wave loads
+  constexpr int LOADS = CPW + 2 * NCL;           // vector-memory ops per lane per k-block
+  static_assert(CPW >= 1 && BM * 8 % (64 * WAVES) == 0, "tile must split evenly over lanes");
+  static_assert(NCL >= 1 && NC % RW == 0, "code loads split evenly over row groups");
   static_assert(S >= 2 && (S - 2) * LOADS < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // S stages
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = wave / NW;                      // row group
+  const int cg = wave % NW;                      // column group
   const int quarter = lane >> 4;
   const int r16 = lane & 15;
 
@@ -108,7 +124,7 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
   int bm, bn;
   tile_of(blockIdx.x, nbm, nbn, &bm, &bn);
   const int row0 = bm * BM;
-  const int tile0 = (bn * NW + wave) * NC;
+  const int tile0 = (bn * NW + cg) * NC;
 
   // Loads go through buffer resources: the base is wave-uniform (scalar
   // registers), each lane adds one fixed 32-bit offset and each k-block one
@@ -121,10 +137,12 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
       p.meta + size_t(tlo) * 16 * p.meta_row_bytes, uint32_t(NC) * 16u * uint32_t(p.meta_row_bytes));
   const uint32_t q_lane = uint32_t(lane) * 16;
   const uint32_t m_lane = uint32_t(r16) * uint32_t(p.meta_row_bytes);
-  uint32_t q_tile[NC], m_tile[NC];                              // clamped column tiles
+  // this wave loads the codes and meta of column tiles rg * NCL + [0, NCL)
+  // of its column group (clamped); the other row groups load the rest
+  uint32_t q_tile[NCL], m_tile[NCL];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = min(tile0 + c, ntiles - 1) - tlo;
+  for (int c = 0; c < NCL; ++c) {
+    const int t = min(tile0 + rg * NCL + c, ntiles - 1) - tlo;
     q_tile[c] = uint32_t(t) * uint32_t(kblocks) * 1024u;
     m_tile[c] = uint32_t(t) * 16u * uint32_t(p.meta_row_bytes);
   }
@@ -142,13 +160,15 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
     const int lchunk = (s & 7) ^ (row & 7);
     a_lane[j] = uint32_t(min(row0 + row, p.m - 1) - row0) * uint32_t(p.lda8) + uint32_t(lchunk * 16);
   }
-  // operand reads: row i*16 + r16, logical chunk 4h + quarter
+  // operand reads: row (rg * MR + i) * 16 + r16, logical chunk 4h + quarter
   int a_off[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) a_off[h] = r16 * 128 + (((4 * h + quarter) ^ (r16 & 7)) * 16);
-  // this wave's weight codes and meta inside a stage (lane-linear, as loaded)
-  const int w_off = A_BYTES + wave * NC * 1024 + lane * 16;
-  const int m_off = A_BYTES + W_BYTES + wave * NC * 256 + lane * 4;
+  for (int h = 0; h < 2; ++h)
+    a_off[h] = rg * (16 * MR * 128) + r16 * 128 + (((4 * h + quarter) ^ (r16 & 7)) * 16);
+  // the weight codes and meta of this wave's column group inside a stage
+  // (lane-linear, as loaded)
+  const int w_off = A_BYTES + cg * NC * 1024 + lane * 16;
+  const int m_off = A_BYTES + W_BYTES + cg * NC * 256 + lane * 4;
 
   v4i acc[MR][NC];
 #pragma unroll
@@ -163,12 +183,12 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
     for (int j = 0; j < CPW; ++j)
       buffer_to_lds16(a_rsrc, st + (wave * CPW + j) * 1024, a_lane[j], uint32_t(kb) * 128u);
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      buffer_to_lds16(q_rsrc, st + A_BYTES + (wave * NC + c) * 1024, q_lane,
+    for (int c = 0; c < NCL; ++c)
+      buffer_to_lds16(q_rsrc, st + A_BYTES + (cg * NC + rg * NCL + c) * 1024, q_lane,
                       q_tile[c] + uint32_t(kb) * 1024u);
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      buffer_to_lds4(m_rsrc, st + A_BYTES + W_BYTES + (wave * NC + c) * 256, m_lane,
+    for (int c = 0; c < NCL; ++c)
+      buffer_to_lds4(m_rsrc, st + A_BYTES + W_BYTES + (cg * NC + rg * NCL + c) * 256, m_lane,
                      m_tile[c] + (GPB == 0 ? 0u : uint32_t((kb * GPB) >> 2) * 4u));
   };
 
@@ -228,46 +248,45 @@ __global__ __launch_bounds__(64 * NW, 2) void tiled_kernel(GemmParams p) {
   // scales are fetched only now: this kernel runs long enough that one
   // more round trip at the end does not matter, and keeping them live
   // through the K loop would cost registers
-  const EpiScales<MR, NC> es = load_scales<MR, NC>(p, row0 / 16, tile0, lane);
+  const int rt0 = row0 / 16 + rg * MR;           // first row tile of this wave
+  const EpiScales<MR, NC> es = load_scales<MR, NC>(p, rt0, tile0, lane);
 #pragma unroll
   for (int i = 0; i < MR; ++i)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (tile0 + c >= ntiles) continue;
       int32_t v[4] = {acc[i][c][0], acc[i][c][1], acc[i][c][2], acc[i][c][3]};
-      store_frag(p, row0 + i * 16, (tile0 + c) * 16, lane, v, es.s1[c], es.sa[i]);
+      store_frag(p, (rt0 + i) * 16, (tile0 + c) * 16, lane, v, es.s1[c], es.sa[i]);
     }
 }
 
-template <int MR, int NC, int GPB, int S>
+template <int MR, int NC, int RW, int GPB, int S>
 hipError_t launch_tiled_t(const GemmParams& p, hipStream_t stream) {
-  constexpr int NW = 4;
-  constexpr int STAGE = 16 * MR * 128 + NW * NC * (1024 + 256);
-  const void* fn = reinterpret_cast<const void*>(&tiled_kernel<MR, NC, NW, GPB, S>);
-  const size_t lds = size_t(S) * STAGE;
+  const void* fn = reinterpret_cast<const void*>(&tiled_kernel<MR, NC, RW, GPB, S>);
+  const size_t lds = size_t(S) * tiled_stage_bytes<MR, NC, RW>();
   if (lds > 65536) {
-    // above the default dynamic-LDS limit: opt in once (the attribute is
-    // per kernel and process-wide, setting it again is harmless)
+    // above the default dynamic-LDS limit: opt in (the attribute is per
+    // kernel and process-wide, setting it again is harmless)
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
   const int ntiles = p.n / 16;
-  const int nbm = (p.m + 16 * MR - 1) / (16 * MR);
-  const int nbn = (ntiles + NW * NC - 1) / (NW * NC);
+  const int nbm = (p.m + RW * 16 * MR - 1) / (RW * 16 * MR);
+  const int nbn = (ntiles + kColGroups * NC - 1) / (kColGroups * NC);
   dim3 grid(nbm * nbn);
-  dim3 block(64 * NW);
+  dim3 block(64 * kColGroups * RW);
   GemmParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel(fn, grid, block, args, lds, stream);
 }
 
-template <int MR, int NC, int S>
+template <int MR, int NC, int RW, int S>
 hipError_t tiled_by_gpb(const GemmParams& p, int gpb, hipStream_t s) {
   switch (gpb) {
-    case 0: return launch_tiled_t<MR, NC, 0, S>(p, s);
-    case 1: return launch_tiled_t<MR, NC, 1, S>(p, s);
-    case 2: return launch_tiled_t<MR, NC, 2, S>(p, s);
-    case 4: return launch_tiled_t<MR, NC, 4, S>(p, s);
+    case 0: return launch_tiled_t<MR, NC, RW, 0, S>(p, s);
+    case 1: return launch_tiled_t<MR, NC, RW, 1, S>(p, s);
+    case 2: return launch_tiled_t<MR, NC, RW, 2, S>(p, s);
+    case 4: return launch_tiled_t<MR, NC, RW, 4, S>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -275,22 +294,25 @@ hipError_t tiled_by_gpb(const GemmParams& p, int gpb, hipStream_t s) {
 }  // namespace
 
 bool tiled_config_supported(const TiledConfig& c) {
-  const bool stages_ok = c.stages == 0 || c.stages == 2 || c.stages == 3;
-  return c.nw == 4 && stages_ok &&
+  if (c.nw != kColGroups) return false;
+  if (c.rw == 2) return c.mr == 8 && c.nc == 4 && c.stages == 3;
+  const bool stages_ok = c.stages == 2 || c.stages == 3;
+  return c.rw == 1 && stages_ok &&
          ((c.mr == 8 && c.nc == 4) || (c.mr == 4 && c.nc == 4) || (c.mr == 8 && c.nc == 2));
 }
 
 hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
                              hipStream_t stream) {
-  if (c.nw != 4) return hipErrorInvalidValue;
+  if (!tiled_config_supported(c)) return hipErrorInvalidValue;
+  if (c.rw == 2) return tiled_by_gpb<8, 4, 2, 3>(p, gpb, stream);
   if (c.stages == 3) {
-    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 3>(p, gpb, stream);
-    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 3>(p, gpb, stream);
-    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 3>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 3>(p, gpb, stream);
+    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 3>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 3>(p, gpb, stream);
   } else {
-    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 2>(p, gpb, stream);
-    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 2>(p, gpb, stream);
-    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 2>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 2>(p, gpb, stream);
+    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 2>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 2>(p, gpb, stream);
   }
   return hipErrorInvalidValue;
 }
