@@ -217,7 +217,9 @@ def main():
         a8 = torch.empty((m, k), dtype=torch.int8, device=dev)
         s_a = torch.empty((m,), dtype=torch.float16, device=dev)
         y = torch.empty((m, n), dtype=torch.float16, device=dev)
-        bufs.append((a, a8, s_a, y))
+        ws_bytes = int(w4.lib.w4a8_gemm_workspace_size(m, n, k, g, None))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        bufs.append((a, a8, s_a, y, ws))
 
     nr = len(runs)
 
@@ -225,11 +227,11 @@ def main():
 
     def launch_step(copy, record=None):
         for r, (m, layer, n, k, g, _) in enumerate(runs):
-            a, a8, s_a, y = bufs[r]
+            a, a8, s_a, y, ws = bufs[r]
             w4.quant_act(a, a8=a8, s_a=s_a)
             if record is not None:
                 record[r][0].record(stream_ptr)
-            w4.gemm(a8, s_a, copy[(layer, g)], n, k, g, y=y)
+            w4.gemm(a8, s_a, copy[(layer, g)], n, k, g, y=y, workspace=ws)
             if record is not None:
                 record[r][1].record(stream_ptr)
 

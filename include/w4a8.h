@@ -129,27 +129,38 @@ w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
  *   y_dev     m x n fp16 output, row stride ldy elements (ldy >= n)
  *   acc_dev   optional (may be NULL): m x n int32 raw accumulators, row
  *             stride ldacc elements (ldacc >= n)
- *   workspace_dev / workspace_bytes: scratch of at least
- *             w4a8_gemm_workspace_size(m, n, k, g) bytes (may be NULL when
- *             that size is 0)
+ *   workspace_dev / workspace_bytes: 16-byte aligned device scratch of at
+ *             least w4a8_gemm_workspace_size(m, n, k, g, opts) bytes (the
+ *             same opts); may be NULL when that size is 0.  Owned by the
+ *             caller; it needs no initialisation, the call overwrites it,
+ *             and two calls in flight at once need two workspaces.
  *   opts      NULL for the automatic choice; otherwise forces the kernel
  *             variant and its split of K (tests and sweeps only).  Results
- *             are identical for every choice.
+ *             are identical for every choice: integer partial sums are
+ *             added exactly.
  * m == 0 is a no-op.  Errors: INVALID_ARGUMENT, UNSUPPORTED (k % 128, n % 16,
  * k > W4A8_K_MAX, bad g), BUFFER_TOO_SMALL, DEVICE. */
 typedef struct {
   int variant;   /* 0 auto, 1 skinny (intra-workgroup split-K), 2 tiled */
-  int k_split;   /* skinny: waves that share one K range (1..8), 0 = auto */
+  int k_split;   /* skinny: waves that split K inside a workgroup (1..8);
+                    tiled: wave groups that split the k-blocks inside a
+                    workgroup (1, or 2 with m_tiles 4 or 8, 2 stages);
+                    0 = auto */
   int n_tiles;   /* 16-column tiles per wave: skinny 1, 2 or 4; tiled 2 or 4; 0 = auto */
   int m_tiles;   /* tiled: 16-row tiles per wave (4 or 8), 0 = auto */
   int stages;    /* tiled: LDS pipeline stages (2 or 3), 0 = auto */
   int row_groups;/* tiled: waves along M per workgroup: 1 (4 waves) or 2
                     (8 waves, 256 x 256 tiles, m_tiles 8 and 3 stages only),
                     0 = auto */
-  int reserved[2];
+  int slices;    /* tiled: workgroups that split K of one tile (1..16), their
+                    int32 partial sums going through the workspace, which
+                    must then hold slices * m * n * 4 bytes; 0 = auto */
+  int reserved;
 } w4a8_gemm_opts;
 
-size_t w4a8_gemm_workspace_size(int m, int n, int k, int g);
+/* Workspace bytes w4a8_gemm needs for these arguments (0 when it needs none,
+ * or when the shape is not supported).  Host only, no HIP call. */
+size_t w4a8_gemm_workspace_size(int m, int n, int k, int g, const w4a8_gemm_opts* opts);
 
 w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
                       int m, const void* blob_dev, int n, int k, int g,

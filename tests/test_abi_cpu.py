@@ -209,8 +209,42 @@ def test_gpu_entry_points_validate_before_any_hip_call():
     opts = w4.GemmOpts(1, 0)
     assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 2   # skinny is M <= 64
     # tiled shapes that do not exist: 8-wave tiles only as 8 x 4 tiles per
-    # wave with 3 stages; row groups 1 or 2; stages 2 or 3
+    # wave with 3 stages (row groups) or 2 stages (k-groups), never both;
+    # row groups and k-groups 1 or 2; stages 2 or 3
     for v, ks, nt, mt, st, rg in ((2, 0, 0, 4, 0, 2), (2, 0, 0, 8, 2, 2), (2, 0, 2, 8, 3, 2),
-                                  (2, 0, 0, 0, 0, 3), (2, 0, 0, 8, 4, 1), (2, 0, 0, 6, 0, 1)):
+                                  (2, 0, 0, 0, 0, 3), (2, 0, 0, 8, 4, 1), (2, 0, 0, 6, 0, 1),
+                                  (2, 3, 0, 0, 0, 0), (2, 2, 2, 8, 0, 0), (2, 2, 0, 8, 3, 0),
+                                  (2, 2, 0, 8, 0, 2)):
         opts = w4.GemmOpts(v, ks, nt, mt, st, rg)
         assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 1, (mt, st, rg)
+    # K split over workgroups: at most 16 slices; the workspace must hold
+    # slices * m * n * 4 bytes and be 16-byte aligned
+    opts = w4.GemmOpts(2, 0, 0, 0, 0, 0, 17)
+    assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 1
+    opts = w4.GemmOpts(2, 0, 0, 0, 0, 0, 2)
+    assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 3          # no workspace
+    need = 2 * 100 * 256 * 4                          # m = 100, n = 256
+    assert call(m=100, lda8=512, ws=ctypes.c_void_p(4096), wsb=need - 1,
+                opts=ctypes.byref(opts)) == 3
+    assert call(m=100, lda8=512, ws=ctypes.c_void_p(4104), wsb=need,
+                opts=ctypes.byref(opts)) == 1                             # misaligned
+
+
+def test_gemm_workspace_size():
+    """Workspace bytes follow the same plan as w4a8_gemm (host only)."""
+    L = w4.lib
+    assert L.w4a8_gemm_workspace_size(16, 4096, 4096, 128, None) == 0       # skinny: none
+    assert L.w4a8_gemm_workspace_size(4096, 8192, 8192, 128, None) == 0     # big grid: none
+    # few 128 x 256 tiles and long K: K split over workgroups, int32 partials
+    need = L.w4a8_gemm_workspace_size(256, 4096, 14336, 128, None)
+    assert need > 0 and need % (256 * 4096 * 4) == 0 and need // (256 * 4096 * 4) in range(2, 9)
+    opts = w4.GemmOpts(2, 0, 0, 0, 0, 0, 3)
+    assert L.w4a8_gemm_workspace_size(100, 256, 1024, 64, ctypes.byref(opts)) == 3 * 100 * 256 * 4
+    opts = w4.GemmOpts(2, 0, 0, 8, 2, 0, 0)                  # forced shape: no automatic split
+    assert L.w4a8_gemm_workspace_size(256, 4096, 14336, 128, ctypes.byref(opts)) == 0
+    opts = w4.GemmOpts(2, 0, 0, 0, 0, 0, 12)                 # more slices than k-blocks: one each
+    assert L.w4a8_gemm_workspace_size(100, 256, 1024, 128, ctypes.byref(opts)) == 8 * 100 * 256 * 4
+    opts = w4.GemmOpts(2, 0, 0, 0, 0, 0, 17)                 # beyond 16 slices: invalid, none
+    assert L.w4a8_gemm_workspace_size(100, 256, 4096, 128, ctypes.byref(opts)) == 0
+    assert L.w4a8_gemm_workspace_size(256, 4096, 14336, 96, None) == 0     # unsupported g
+    assert L.w4a8_gemm_workspace_size(0, 4096, 14336, 128, None) == 0

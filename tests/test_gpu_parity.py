@@ -8,7 +8,7 @@ import pytest
 
 import synth
 import w4a8_gemm_amd as w4
-from gpu_util import log, run_gemm, run_quant_act
+from gpu_util import device, log, run_gemm, run_quant_act
 from oracle import ref
 
 pytestmark = pytest.mark.gpu
@@ -143,14 +143,37 @@ def test_gemm_tiled_every_tile_shape(m, n, k, g):
     row groups per workgroup, stages) on ragged M and N edges."""
     w, a, out = _layer(m, n, k, g, "student_t4", seed=90 + m)
     blob = w4.pack(w, g)
-    for mt, nt, rg, st in ((0, 0, 0, 0), (4, 4, 1, 2), (4, 4, 1, 3), (8, 4, 1, 2), (8, 4, 1, 3),
-                           (8, 2, 1, 3), (8, 4, 2, 0)):
+    for mt, nt, rg, st, ks in ((0, 0, 0, 0, 0), (4, 4, 1, 2, 0), (4, 4, 1, 3, 0), (8, 4, 1, 2, 0),
+                               (8, 4, 1, 3, 0), (8, 2, 1, 3, 0), (8, 4, 2, 0, 0), (8, 4, 1, 0, 2),
+                               (4, 4, 1, 0, 2)):
         log(f"gemm tiled m={m} n={n} k={k} g={g} m_tiles={mt} n_tiles={nt} row_groups={rg} "
-            f"stages={st}")
+            f"stages={st} k_split={ks}")
         y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=2, m_tiles=mt,
-                          n_tiles=nt, row_groups=rg, stages=st)
-        assert np.array_equal(acc, out["acc"]), (mt, nt, rg, st)
+                          n_tiles=nt, row_groups=rg, stages=st, k_split=ks)
+        assert np.array_equal(acc, out["acc"]), (mt, nt, rg, st, ks)
         assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
+@pytest.mark.parametrize("m,n,k,g", [(130, 1040, 1152, 0), (300, 528, 2688, 64), (77, 256, 640, 32)])
+def test_gemm_tiled_k_slices_exact(m, n, k, g):
+    """K split over workgroups: int32 partials through a caller workspace that
+    starts out full of garbage, ragged last slice, with and without k-groups."""
+    import torch
+    w, a, out = _layer(m, n, k, g, "student_t4", seed=700 + m)
+    blob = w4.pack(w, g)
+    dev = device()
+    a8 = torch.from_numpy(out["a8"]).to(dev)
+    s_a = torch.from_numpy(out["s_a"]).to(dev)
+    wdev = w4.to_device(blob, dev)
+    kblocks = k // 128
+    for sl, mt, ks in ((2, 8, 0), (3, 4, 0), (5, 8, 2), (min(kblocks, 16), 4, 2), (16, 8, 0)):
+        ws = torch.full((16 * m * n * 4 + 64,), 0x5A, dtype=torch.uint8, device=dev)
+        log(f"gemm tiled slices={sl} m={m} n={n} k={k} g={g} m_tiles={mt} k_split={ks}")
+        y, acc = w4.gemm(a8, s_a, wdev, n, k, g, want_acc=True, variant=2, m_tiles=mt,
+                         k_split=ks, slices=sl, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), out["acc"]), (sl, mt, ks)
+        assert ref.y_tolerance_ok(y.cpu().numpy(), out["y"]).all()
 
 
 def test_gemm_extreme_operands():

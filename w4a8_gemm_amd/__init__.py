@@ -49,7 +49,7 @@ class GemmOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("k_split", ctypes.c_int),
                 ("n_tiles", ctypes.c_int), ("m_tiles", ctypes.c_int),
                 ("stages", ctypes.c_int), ("row_groups", ctypes.c_int),
-                ("reserved", ctypes.c_int * 2)]
+                ("slices", ctypes.c_int), ("reserved", ctypes.c_int)]
 
 
 def _load():
@@ -72,7 +72,7 @@ def _load():
         "w4a8_blob_info": (I, [P, Z, P, P, P]),
         "w4a8_unpack": (I, [P, Z, P, P, P, P]),
         "w4a8_quant_act": (I, [P, I, I, I, P, I, P, P]),
-        "w4a8_gemm_workspace_size": (Z, [I, I, I, I]),
+        "w4a8_gemm_workspace_size": (Z, [I, I, I, I, P]),
         "w4a8_gemm": (I, [P, I, P, I, P, I, I, I, P, I, P, I, P, Z, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -174,7 +174,7 @@ def quant_act(a, a8=None, s_a=None, stream=None):
 
 def gemm(a8, s_a, blob_dev, n: int, k: int, g: int, y=None, acc=None, want_acc=False,
          variant: int = 0, k_split: int = 0, n_tiles: int = 0, m_tiles: int = 0,
-         stages: int = 0, row_groups: int = 0, workspace=None, stream=None):
+         stages: int = 0, row_groups: int = 0, slices: int = 0, workspace=None, stream=None):
     """Y = fp16(s_a * s1 * (A8 @ W8^.T)); returns y (and the int32 acc if asked)."""
     torch = _torch()
     m = a8.shape[0]
@@ -184,11 +184,12 @@ def gemm(a8, s_a, blob_dev, n: int, k: int, g: int, y=None, acc=None, want_acc=F
     if want_acc and acc is None:
         acc = torch.empty((m, n), dtype=torch.int32, device=a8.device)
     opts = None
-    if variant or k_split or n_tiles or m_tiles or stages or row_groups:
-        opts = GemmOpts(variant, k_split, n_tiles, m_tiles, stages, row_groups)
-    ws_need = int(lib.w4a8_gemm_workspace_size(m, n, k, g))
+    if variant or k_split or n_tiles or m_tiles or stages or row_groups or slices:
+        opts = GemmOpts(variant, k_split, n_tiles, m_tiles, stages, row_groups, slices)
+    ws_need = int(lib.w4a8_gemm_workspace_size(m, n, k, g,
+                                               ctypes.byref(opts) if opts is not None else None))
     if ws_need and workspace is None:
-        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=a8.device)
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=a8.device)
     st = lib.w4a8_gemm(a8.data_ptr(), a8.stride(0), s_a.data_ptr(), m, blob_dev.data_ptr(), n, k,
                        g, y.data_ptr(), y.stride(0),
                        acc.data_ptr() if acc is not None else None,

@@ -86,12 +86,93 @@ extern "C" w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int l
                                         static_cast<hipStream_t>(stream)));
 }
 
-extern "C" size_t w4a8_gemm_workspace_size(int m, int n, int k, int g) {
-  (void)m;
-  (void)n;
-  (void)k;
-  (void)g;
-  return 0;  // both variants reduce split-K partials on chip
+namespace {
+
+// Everything the automatic choice (or a forced one) decides for one call.
+struct Plan {
+  w4a8_status status = W4A8_OK;
+  int variant = 0;          // 1 skinny, 2 tiled
+  SkinnyConfig skinny{};
+  TiledConfig tiled{};
+  int slices = 1;           // tiled: workgroups splitting K (partials in the workspace)
+  int kb_per_slice = 0;
+  size_t workspace = 0;     // bytes
+};
+
+// Tiles of the four-wave and eight-wave tiled kernels.
+long tiled_tiles(int m, int n, int rows) {
+  return long((m + rows - 1) / rows) * long((n / kColTile + 15) / 16);
+}
+
+Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
+  Plan pl;
+  pl.variant = opts ? opts->variant : 0;
+  if (pl.variant < 0 || pl.variant > 2) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
+  if (pl.variant == 0) pl.variant = m <= 64 ? 1 : 2;
+  const int kblocks = k / kKBlock;
+  if (pl.variant == 1) {
+    if (m > 64) { pl.status = W4A8_ERR_UNSUPPORTED; return pl; }
+    SkinnyConfig& c = pl.skinny;
+    c = choose_skinny(m, n, k);
+    if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
+    if (opts && opts->k_split > 0) {
+      c.kw = opts->k_split;
+      c.kbw = blocks_per_wave(kblocks, c.kw);
+    }
+    return pl;
+  }
+  // Tiled (choices from timing sweeps on the layer shapes): 256 x 256 tiles
+  // of eight waves with 3 stages when they fill every compute unit at least
+  // once; else 128 x 256 tiles of four waves with 2 stages (two workgroups
+  // per compute unit) when there are enough of them; else, for at most 64
+  // such tiles or K of at least 8192, the same tiles with K split over 2..8
+  // workgroups so that about 384 workgroups run (each slice keeps at least
+  // 4 k-blocks); else 64 x 256 tiles with 3 stages.
+  TiledConfig& c = pl.tiled;
+  c.nw = 4;
+  c.nc = 4;
+  const long tiles256 = tiled_tiles(m, n, 256);
+  const long tiles128 = tiled_tiles(m, n, 128);
+  c.rw = tiles256 >= 256 ? 2 : 1;
+  c.kg = 1;
+  // a forced row-tile, stage or k-group count without a forced row-group
+  // count selects among the four-wave-per-k-group kernels
+  if (opts && (opts->m_tiles > 0 || opts->stages > 0 || opts->k_split > 0)) c.rw = 1;
+  if (opts && opts->row_groups > 0) c.rw = opts->row_groups;
+  if (opts && opts->k_split > 0) c.kg = opts->k_split;
+  c.mr = (c.rw == 2 || tiles128 >= 192) ? 8 : 4;
+  if (opts && opts->m_tiles > 0) c.mr = opts->m_tiles;
+  c.stages = (c.rw == 2 || (c.mr == 4 && c.kg == 1)) ? 3 : 2;
+  if (opts && opts->stages > 0) c.stages = opts->stages;
+  if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
+  int slices = 1;
+  const bool forced = opts && (opts->m_tiles > 0 || opts->stages > 0 || opts->k_split > 0 ||
+                               opts->row_groups > 0 || opts->n_tiles > 0 || opts->slices > 0);
+  if (!forced && c.rw == 1 && tiles128 < 192 && (tiles128 <= 64 || kblocks >= 64)) {
+    const long want = (384 + tiles128 - 1) / tiles128;
+    const int most = std::min(8, kblocks / 4);
+    if (most >= 2) {
+      slices = int(std::max(2L, std::min<long>(want, most)));
+      c.mr = 8;
+      c.stages = 2;
+    }
+  }
+  if (opts && opts->slices > 0) slices = opts->slices;
+  if (slices > kMaxSlices) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
+  slices = std::min(slices, kblocks);
+  pl.kb_per_slice = (kblocks + slices - 1) / slices;
+  pl.slices = (kblocks + pl.kb_per_slice - 1) / pl.kb_per_slice;   // none empty
+  if (pl.slices > 1) pl.workspace = size_t(pl.slices) * size_t(m) * size_t(n) * 4u;
+  return pl;
+}
+
+}  // namespace
+
+extern "C" size_t w4a8_gemm_workspace_size(int m, int n, int k, int g,
+                                           const w4a8_gemm_opts* opts) {
+  if (m <= 0 || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
+  const Plan pl = plan_gemm(m, n, k, opts);
+  return pl.status == W4A8_OK ? pl.workspace : 0;
 }
 
 extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev, int m,
@@ -99,14 +180,23 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
                                  int ldy, int32_t* acc_dev, int ldacc, void* workspace_dev,
                                  size_t workspace_bytes, const w4a8_gemm_opts* opts,
                                  void* stream) {
-  (void)workspace_dev;
   if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
   if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   if (m == 0) return W4A8_OK;
   if (!a8_dev || !s_a_dev || !blob_dev || !y_dev) return W4A8_ERR_INVALID_ARGUMENT;
   if (lda8 < k || lda8 % 16 || ldy < n || (acc_dev && ldacc < n)) return W4A8_ERR_INVALID_ARGUMENT;
   if (!aligned16(a8_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < w4a8_gemm_workspace_size(m, n, k, g)) return W4A8_ERR_BUFFER_TOO_SMALL;
+
+  const Plan pl = plan_gemm(m, n, k, opts);
+  if (pl.status != W4A8_OK) return pl.status;
+  const int gpb = groups_per_block(k, g);
+  if (pl.variant == 1 && !skinny_config_supported(pl.skinny, k, gpb))
+    return W4A8_ERR_INVALID_ARGUMENT;
+  if (pl.variant == 2 && !tiled_config_supported(pl.tiled)) return W4A8_ERR_INVALID_ARGUMENT;
+  if (pl.workspace) {
+    if (!workspace_dev || workspace_bytes < pl.workspace) return W4A8_ERR_BUFFER_TOO_SMALL;
+    if (!aligned16(workspace_dev)) return W4A8_ERR_INVALID_ARGUMENT;
+  }
 
   Sections sec = sections(n, k, g);
   const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
@@ -122,51 +212,24 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
   p.k = k;
   p.meta_row_bytes = sec.meta_row_bytes;
   p.kb_per_wave = 0;
-  const int gpb = groups_per_block(k, g);
   p.y = y_dev;
   p.ldy = ldy;
   p.acc = acc_dev;
   p.ldacc = acc_dev ? ldacc : 0;
+  p.part = nullptr;
+  p.kb_per_slice = k / kKBlock;
 
-  int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant > 2) return W4A8_ERR_INVALID_ARGUMENT;
-  if (variant == 0) variant = m <= 64 ? 1 : 2;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (variant == 1) {
-    if (m > 64) return W4A8_ERR_UNSUPPORTED;
-    SkinnyConfig c = choose_skinny(m, n, k);
-    if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
-    if (opts && opts->k_split > 0) {
-      c.kw = opts->k_split;
-      c.kbw = blocks_per_wave(k / kKBlock, c.kw);
-    }
-    if (!skinny_config_supported(c, k, gpb)) return W4A8_ERR_INVALID_ARGUMENT;
-    e = launch_gemm_skinny(p, gpb, c, s);
+  if (pl.variant == 1) {
+    e = launch_gemm_skinny(p, gpb, pl.skinny, s);
   } else {
-    // Tiled (choices from timing sweeps on the layer shapes): 256 x 256
-    // tiles of eight waves with 3 stages when they fill every compute unit
-    // at least once; else 128 x 256 tiles of four waves with 2 stages (two
-    // workgroups per compute unit) when there are enough of them; else
-    // 64 x 256 tiles with 3 stages.
-    TiledConfig c;
-    c.nw = 4;
-    c.nc = 4;
-    const long col256 = long((n / kColTile + 15) / 16);
-    const long tiles256 = long((m + 255) / 256) * col256;
-    const long tiles128 = long((m + 127) / 128) * col256;
-    c.rw = tiles256 >= 256 ? 2 : 1;
-    // a forced row-tile count or stage count without a forced row-group
-    // count selects among the four-wave kernels
-    if (opts && (opts->m_tiles > 0 || opts->stages > 0)) c.rw = 1;
-    if (opts && opts->row_groups > 0) c.rw = opts->row_groups;
-    c.mr = (c.rw == 2 || tiles128 >= 192) ? 8 : 4;
-    if (opts && opts->m_tiles > 0) c.mr = opts->m_tiles;
-    c.stages = (c.rw == 2 || c.mr == 4) ? 3 : 2;
-    if (opts && opts->stages > 0) c.stages = opts->stages;
-    if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
-    if (!tiled_config_supported(c)) return W4A8_ERR_INVALID_ARGUMENT;
-    e = launch_gemm_tiled(p, gpb, c, s);
+    if (pl.slices > 1) {
+      p.part = static_cast<int32_t*>(workspace_dev);
+      p.kb_per_slice = pl.kb_per_slice;
+    }
+    e = launch_gemm_tiled(p, gpb, pl.tiled, pl.slices, s);
+    if (e == hipSuccess && pl.slices > 1) e = launch_split_reduce(p, pl.slices, s);
   }
   return device_status(e);
 }

@@ -21,7 +21,11 @@ struct GemmParams {
   int32_t* acc;          // optional raw accumulators
   int ldacc;
   int kb_per_wave;       // skinny: 128-k blocks per wave (a multiple of 4 / groups-per-block)
+  int32_t* part;         // tiled, K split over workgroups: slices x m x n int32 partial sums
+  int kb_per_slice;      // tiled: 128-k blocks per K slice (all of K when not split)
 };
+
+constexpr int kMaxSlices = 16;   // workgroups splitting K of one tile
 
 // Groups per 128-k block: 1, 2 or 4 for g = 128, 64, 32; 0 in per-channel mode.
 inline int groups_per_block(int k, int g) {
@@ -41,6 +45,7 @@ struct TiledConfig {
   int nc;       // 16-column tiles per wave
   int nw;       // waves along N per workgroup (4)
   int rw;       // waves along M per workgroup (1, or 2 for 256 x 256 tiles)
+  int kg;       // wave groups splitting the k-blocks inside a workgroup (1 or 2)
   int stages;   // LDS pipeline stages (2 or 3)
 };
 
@@ -48,8 +53,12 @@ hipError_t launch_quant_act(const uint16_t* a, int m, int k, int lda, int8_t* a8
                             uint16_t* s_a, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmParams& p, int gpb, const SkinnyConfig& c,
                               hipStream_t stream);
-hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
+// slices > 1: workgroup (tile, slice) covers k-blocks [slice * kb_per_slice,
+// +kb_per_slice) and writes its raw int32 tile to p.part; launch_split_reduce
+// then adds the slices and applies the epilogue.
+hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c, int slices,
                              hipStream_t stream);
+hipError_t launch_split_reduce(const GemmParams& p, int slices, hipStream_t stream);
 bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb);
 bool tiled_config_supported(const TiledConfig& c);
 

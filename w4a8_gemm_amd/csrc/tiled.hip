@@ -87,33 +87,44 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int* bm, int*
 
 constexpr int kColGroups = 4;   // waves along N per workgroup
 
-template <int MR, int NC, int RW>
+// One LDS stage: for each of the KG k-groups, the activation tile, weight
+// codes and meta of one k-block.
+template <int MR, int NC, int RW, int KG>
 constexpr int tiled_stage_bytes() {
-  return RW * 16 * MR * 128 + kColGroups * NC * (1024 + 256);
+  return KG * (RW * 16 * MR * 128 + kColGroups * NC * (1024 + 256));
 }
 
-template <int MR, int NC, int RW, int GPB, int S>
-__global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(GemmParams p) {
+// RW row groups x KG k-groups x 4 column groups of waves.  With KG = 2 the
+// two k-groups take alternate k-blocks of the same tile (an exact split of
+// K inside the workgroup) and add their int32 tiles through LDS at the end.
+template <int MR, int NC, int RW, int KG, int GPB, int S>
+__global__ __launch_bounds__(64 * kColGroups * RW * KG, 2 / (RW * KG)) void tiled_kernel(
+    GemmParams p) {
+  static_assert(RW * KG <= 2, "at most eight waves (two per SIMD)");
   constexpr int NW = kColGroups;
-  constexpr int WAVES = NW * RW;
+  constexpr int KWAVES = NW * RW;                // waves of one k-group
   constexpr int BM = RW * 16 * MR;
   constexpr int A_BYTES = BM * 128;              // activation tile of one k-block
   constexpr int W_BYTES = NW * NC * 1024;        // weight codes of one k-block
   constexpr int M_BYTES = NW * NC * 256;         // meta dwords of one k-block
-  constexpr int STAGE = A_BYTES + W_BYTES + M_BYTES;
-  static_assert(STAGE == tiled_stage_bytes<MR, NC, RW>(), "stage layout");
-  constexpr int CPW = BM * 8 / (64 * WAVES);     // activation chunks per lane
+  constexpr int SUB = A_BYTES + W_BYTES + M_BYTES;
+  constexpr int STAGE = KG * SUB;
+  static_assert(STAGE == tiled_stage_bytes<MR, NC, RW, KG>(), "stage layout");
+  constexpr int CPW = BM * 8 / (64 * KWAVES);    // activation chunks per lane
   constexpr int NCL = NC / RW;                   // column tiles whose codes this wave loads
-  constexpr int LOADS = CPW + 2 * NCL;           // vector-memory ops per lane per k-block
-  static_assert(CPW >= 1 && BM * 8 % (64 * WAVES) == 0, "tile must split evenly over lanes");
+  constexpr int LOADS = CPW + 2 * NCL;           // vector-memory ops per lane per stage
+  static_assert(CPW >= 1 && BM * 8 % (64 * KWAVES) == 0, "tile must split evenly over lanes");
   static_assert(NCL >= 1 && NC % RW == 0, "code loads split evenly over row groups");
   static_assert(S >= 2 && (S - 2) * LOADS < 64, "vmcnt range");
+  static_assert(KG == 1 || S * STAGE >= KWAVES * MR * NC * 1024, "LDS holds the k-group sum");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // S stages
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = wave / NW;                      // row group
   const int cg = wave % NW;                      // column group
+  const int rg = (wave / NW) % RW;               // row group
+  const int kg = wave / KWAVES;                  // k-group
+  const int wk = wave % KWAVES;                  // wave inside its k-group
   const int quarter = lane >> 4;
   const int r16 = lane & 15;
 
@@ -121,8 +132,12 @@ __global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(Gem
   const int kblocks = p.k >> 7;
   const int nbm = (p.m + BM - 1) / BM;
   const int nbn = (ntiles + NW * NC - 1) / (NW * NC);
+  // K slice of this workgroup: k-blocks [kb0, kb1)
+  const int slice = blockIdx.x / (nbm * nbn);
+  const int kb0 = slice * p.kb_per_slice;
+  const int kb1 = min(kblocks, kb0 + p.kb_per_slice);
   int bm, bn;
-  tile_of(blockIdx.x, nbm, nbn, &bm, &bn);
+  tile_of(blockIdx.x - slice * (nbm * nbn), nbm, nbn, &bm, &bn);
   const int row0 = bm * BM;
   const int tile0 = (bn * NW + cg) * NC;
 
@@ -147,7 +162,7 @@ __global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(Gem
     m_tile[c] = uint32_t(t) * 16u * uint32_t(p.meta_row_bytes);
   }
   // Activation tile: instruction j of this wave fills 16-byte slots
-  // [(wave * CPW + j) * 64, +64); slot s holds row s / 8, physical chunk
+  // [(wk * CPW + j) * 64, +64); slot s holds row s / 8, physical chunk
   // s % 8, i.e. logical chunk (s % 8) ^ (row % 8).  Offsets are relative to
   // row0 (rows past M read row M - 1, whose results are never stored).
   const __amdgpu_buffer_rsrc_t a_rsrc =
@@ -155,7 +170,7 @@ __global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(Gem
   uint32_t a_lane[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
-    const int s = (wave * CPW + j) * 64 + lane;
+    const int s = (wk * CPW + j) * 64 + lane;
     const int row = s >> 3;
     const int lchunk = (s & 7) ^ (row & 7);
     a_lane[j] = uint32_t(min(row0 + row, p.m - 1) - row0) * uint32_t(p.lda8) + uint32_t(lchunk * 16);
@@ -164,11 +179,12 @@ __global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(Gem
   int a_off[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    a_off[h] = rg * (16 * MR * 128) + r16 * 128 + (((4 * h + quarter) ^ (r16 & 7)) * 16);
+    a_off[h] = kg * SUB + rg * (16 * MR * 128) + r16 * 128 +
+               (((4 * h + quarter) ^ (r16 & 7)) * 16);
   // the weight codes and meta of this wave's column group inside a stage
   // (lane-linear, as loaded)
-  const int w_off = A_BYTES + cg * NC * 1024 + lane * 16;
-  const int m_off = A_BYTES + W_BYTES + cg * NC * 256 + lane * 4;
+  const int w_off = kg * SUB + A_BYTES + cg * NC * 1024 + lane * 16;
+  const int m_off = kg * SUB + A_BYTES + W_BYTES + cg * NC * 256 + lane * 4;
 
   v4i acc[MR][NC];
 #pragma unroll
@@ -176,12 +192,13 @@ __global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(Gem
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[i][c] = v4i{0, 0, 0, 0};
 
-  // every load of k-block kb goes straight to LDS stage `stage`
+  // every load of k-block kb goes straight to this k-group's part of LDS
+  // stage `stage`
   auto issue = [&](int kb, int stage) {
-    uint8_t* st = smem + stage * STAGE;
+    uint8_t* st = smem + stage * STAGE + kg * SUB;
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
-      buffer_to_lds16(a_rsrc, st + (wave * CPW + j) * 1024, a_lane[j], uint32_t(kb) * 128u);
+      buffer_to_lds16(a_rsrc, st + (wk * CPW + j) * 1024, a_lane[j], uint32_t(kb) * 128u);
 #pragma unroll
     for (int c = 0; c < NCL; ++c)
       buffer_to_lds16(q_rsrc, st + A_BYTES + (cg * NC + rg * NCL + c) * 1024, q_lane,
@@ -230,40 +247,103 @@ __global__ __launch_bounds__(64 * kColGroups * RW, 2 / RW) void tiled_kernel(Gem
     }
   };
 
-  // Pipeline of depth S - 1: at iteration kb the loads of k-blocks
-  // kb + 1 .. kb + S - 2 are in flight; block kb + S - 1 is issued into the
-  // stage that iteration kb - 1 consumed, after the barrier that proves
-  // every wave is done with it.  Loads past the end re-read the last block
-  // into a stage that is never read again, so the loop has no branch.
+  // Pipeline of depth S - 1 over super-blocks of KG k-blocks (k-group kg
+  // takes k-block kb0 + sb * KG + kg): at iteration sb the loads of super-blocks
+  // sb + 1 .. sb + S - 2 are in flight; super-block sb + S - 1 is issued
+  // into the stage that iteration sb - 1 consumed, after the barrier that
+  // proves every wave is done with it.  Loads past the end re-read the last
+  // k-block into a part of a stage whose results are never used, so the
+  // loop has no branch around the loads.
+  const int nsb = (kb1 - kb0 + KG - 1) / KG;
 #pragma unroll
-  for (int j = 0; j < S - 1; ++j) issue(min(j, kblocks - 1), j);
-  for (int kb = 0; kb < kblocks; ++kb) {
-    wait_vm<(S - 2) * LOADS>();    // this wave's loads of block kb have landed
+  for (int j = 0; j < S - 1; ++j) issue(min(kb0 + j * KG + kg, kb1 - 1), j);
+  for (int sb = 0; sb < nsb; ++sb) {
+    wait_vm<(S - 2) * LOADS>();    // this wave's loads of super-block sb have landed
     __builtin_amdgcn_s_barrier();  // ... and every other wave's share of the tile
-    issue(min(kb + S - 1, kblocks - 1), (kb + S - 1) % S);
-    compute(kb, smem + (kb % S) * STAGE);
+    issue(min(kb0 + (sb + S - 1) * KG + kg, kb1 - 1), (sb + S - 1) % S);
+    const int kb = kb0 + sb * KG + kg;
+    if (KG == 1 || kb < kb1) compute(kb, smem + (sb % S) * STAGE);
   }
   wait_vm<0>();                    // no LDS write still in flight at exit
+
+  if (KG == 2) {
+    // k-group 1 hands its int32 tile to k-group 0 through LDS (exact sum)
+    __syncthreads();               // every wave is done reading the stages
+    v4i* red = reinterpret_cast<v4i*>(smem) + wk * (MR * NC * 64) + lane;
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) red[(i * NC + c) * 64] = acc[i][c];
+    }
+    __syncthreads();
+    if (kg == 1) return;
+  }
 
   // scales are fetched only now: this kernel runs long enough that one
   // more round trip at the end does not matter, and keeping them live
   // through the K loop would cost registers
   const int rt0 = row0 / 16 + rg * MR;           // first row tile of this wave
+  if (p.part) {
+    // K split over workgroups: raw partial sums, added by split_reduce_kernel
+    int32_t* part = p.part + size_t(slice) * size_t(p.m) * size_t(p.n);
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int col = (tile0 + c) * 16 + r16;
+        if (tile0 + c >= ntiles) continue;
+        v4i t = acc[i][c];
+        if (KG == 2)
+          t += reinterpret_cast<const v4i*>(smem)[wk * (MR * NC * 64) + (i * NC + c) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = (rt0 + i) * 16 + 4 * quarter + r;
+          if (row < p.m) part[size_t(row) * p.n + col] = t[r];
+        }
+      }
+    return;
+  }
   const EpiScales<MR, NC> es = load_scales<MR, NC>(p, rt0, tile0, lane);
 #pragma unroll
   for (int i = 0; i < MR; ++i)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (tile0 + c >= ntiles) continue;
-      int32_t v[4] = {acc[i][c][0], acc[i][c][1], acc[i][c][2], acc[i][c][3]};
+      v4i t = acc[i][c];
+      if (KG == 2)   // plus k-group 1's share, left in LDS above
+        t += reinterpret_cast<const v4i*>(smem)[wk * (MR * NC * 64) + (i * NC + c) * 64 + lane];
+      int32_t v[4] = {t[0], t[1], t[2], t[3]};
       store_frag(p, (rt0 + i) * 16, (tile0 + c) * 16, lane, v, es.s1[c], es.sa[i]);
     }
 }
 
-template <int MR, int NC, int RW, int GPB, int S>
-hipError_t launch_tiled_t(const GemmParams& p, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&tiled_kernel<MR, NC, RW, GPB, S>);
-  const size_t lds = size_t(S) * tiled_stage_bytes<MR, NC, RW>();
+// Sum of the K slices' int32 partial tiles (exact) and the epilogue
+// Y = fp16((acc * s_a) * s1).  One thread per 4 consecutive outputs, so the
+// partial rows are read with coalesced 16-byte loads.
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmParams p, int slices) {
+  const int n4 = p.n >> 2;
+  const long idx = long(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= long(p.m) * n4) return;
+  const int row = int(idx / n4);
+  const int col = int(idx - long(row) * n4) * 4;
+  const size_t plane = size_t(p.m) * size_t(p.n);
+  const v4i* src = reinterpret_cast<const v4i*>(p.part + size_t(row) * p.n + col);
+  v4i t = src[0];
+  for (int sl = 1; sl < slices; ++sl) t += src[sl * (plane >> 2)];
+  const float sa = h2f(p.s_a[row]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float y = (static_cast<float>(t[j]) * sa) * h2f(p.s1[col + j]);
+    p.y[size_t(row) * p.ldy + col + j] = f2h_bits(y);
+    if (p.acc) p.acc[size_t(row) * p.ldacc + col + j] = t[j];
+  }
+}
+
+template <int MR, int NC, int RW, int KG, int GPB, int S>
+hipError_t launch_tiled_t(const GemmParams& p, int slices, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&tiled_kernel<MR, NC, RW, KG, GPB, S>);
+  const size_t lds = size_t(S) * tiled_stage_bytes<MR, NC, RW, KG>();
   if (lds > 65536) {
     // above the default dynamic-LDS limit: opt in (the attribute is per
     // kernel and process-wide, setting it again is harmless)
@@ -273,20 +353,20 @@ hipError_t launch_tiled_t(const GemmParams& p, hipStream_t stream) {
   const int ntiles = p.n / 16;
   const int nbm = (p.m + RW * 16 * MR - 1) / (RW * 16 * MR);
   const int nbn = (ntiles + kColGroups * NC - 1) / (kColGroups * NC);
-  dim3 grid(nbm * nbn);
-  dim3 block(64 * kColGroups * RW);
+  dim3 grid(nbm * nbn * slices);
+  dim3 block(64 * kColGroups * RW * KG);
   GemmParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel(fn, grid, block, args, lds, stream);
 }
 
-template <int MR, int NC, int RW, int S>
-hipError_t tiled_by_gpb(const GemmParams& p, int gpb, hipStream_t s) {
+template <int MR, int NC, int RW, int KG, int S>
+hipError_t tiled_by_gpb(const GemmParams& p, int gpb, int sl, hipStream_t s) {
   switch (gpb) {
-    case 0: return launch_tiled_t<MR, NC, RW, 0, S>(p, s);
-    case 1: return launch_tiled_t<MR, NC, RW, 1, S>(p, s);
-    case 2: return launch_tiled_t<MR, NC, RW, 2, S>(p, s);
-    case 4: return launch_tiled_t<MR, NC, RW, 4, S>(p, s);
+    case 0: return launch_tiled_t<MR, NC, RW, KG, 0, S>(p, sl, s);
+    case 1: return launch_tiled_t<MR, NC, RW, KG, 1, S>(p, sl, s);
+    case 2: return launch_tiled_t<MR, NC, RW, KG, 2, S>(p, sl, s);
+    case 4: return launch_tiled_t<MR, NC, RW, KG, 4, S>(p, sl, s);
   }
   return hipErrorInvalidValue;
 }
@@ -295,26 +375,43 @@ hipError_t tiled_by_gpb(const GemmParams& p, int gpb, hipStream_t s) {
 
 bool tiled_config_supported(const TiledConfig& c) {
   if (c.nw != kColGroups) return false;
-  if (c.rw == 2) return c.mr == 8 && c.nc == 4 && c.stages == 3;
+  if (c.rw == 2) return c.kg == 1 && c.mr == 8 && c.nc == 4 && c.stages == 3;
+  if (c.kg == 2) return c.rw == 1 && (c.mr == 8 || c.mr == 4) && c.nc == 4 && c.stages == 2;
   const bool stages_ok = c.stages == 2 || c.stages == 3;
-  return c.rw == 1 && stages_ok &&
+  return c.rw == 1 && c.kg == 1 && stages_ok &&
          ((c.mr == 8 && c.nc == 4) || (c.mr == 4 && c.nc == 4) || (c.mr == 8 && c.nc == 2));
 }
 
-hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
+hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c, int sl,
                              hipStream_t stream) {
-  if (!tiled_config_supported(c)) return hipErrorInvalidValue;
-  if (c.rw == 2) return tiled_by_gpb<8, 4, 2, 3>(p, gpb, stream);
+  if (!tiled_config_supported(c) || sl < 1 || sl > kMaxSlices) return hipErrorInvalidValue;
+  if (sl > 1 && (p.part == nullptr || p.kb_per_slice * (sl - 1) >= p.k / 128))
+    return hipErrorInvalidValue;
+  if (c.rw == 2) return tiled_by_gpb<8, 4, 2, 1, 3>(p, gpb, sl, stream);
+  if (c.kg == 2) {
+    if (c.mr == 8) return tiled_by_gpb<8, 4, 1, 2, 2>(p, gpb, sl, stream);
+    return tiled_by_gpb<4, 4, 1, 2, 2>(p, gpb, sl, stream);
+  }
   if (c.stages == 3) {
-    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 3>(p, gpb, stream);
-    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 3>(p, gpb, stream);
-    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 3>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 1, 3>(p, gpb, sl, stream);
+    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 1, 3>(p, gpb, sl, stream);
+    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 1, 3>(p, gpb, sl, stream);
   } else {
-    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 2>(p, gpb, stream);
-    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 2>(p, gpb, stream);
-    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 2>(p, gpb, stream);
+    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 1, 2>(p, gpb, sl, stream);
+    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 1, 2>(p, gpb, sl, stream);
+    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 1, 2>(p, gpb, sl, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_reduce(const GemmParams& p, int slices, hipStream_t stream) {
+  if (p.part == nullptr || p.n % 4 || slices < 1) return hipErrorInvalidValue;
+  const long threads = long(p.m) * (p.n / 4);
+  GemmParams arg = p;
+  int sl = slices;
+  void* args[] = {&arg, &sl};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&split_reduce_kernel),
+                         dim3(unsigned((threads + 255) / 256)), dim3(256), args, 0, stream);
 }
 
 }  // namespace w4a8
