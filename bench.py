@@ -1,8 +1,9 @@
 """Benchmark of the W4A8 linear layer on one MI355X.
 
 One step = one pass of the whole hot path over a workload: for every run
-(M, layer) of the workload, the per-token activation quantizer followed by
-the W4A8 GEMM, each through the C ABI library.  Inputs are resident in HBM
+(M, layer) of the workload, the per-token activation quantizer and the W4A8
+GEMM through the C ABI library (one fused launch, w4a8_linear, where M is
+small enough; else w4a8_quant_act then w4a8_gemm).  Inputs are resident in HBM
 when the timed region starts.  Weight blobs rotate through a pool of copies
 of at least 1 GiB so that every GEMM reads its weights from HBM rather than
 from the 256 MB Infinity Cache or the L2.
@@ -225,13 +226,22 @@ def main():
 
     stream_ptr = int(torch.cuda.current_stream().cuda_stream)
 
+    # small M: quantization fused into the GEMM (one launch, w4a8_linear);
+    # else the quantizer, then the GEMM; events bracket the GEMM launch
+    fused = [int(w4.lib.w4a8_linear_launches(m, n, k, g, None)) == 1
+             for (m, _, n, k, g, _) in runs]
+
     def launch_step(copy, record=None):
         for r, (m, layer, n, k, g, _) in enumerate(runs):
             a, a8, s_a, y, ws = bufs[r]
-            w4.quant_act(a, a8=a8, s_a=s_a)
+            if not fused[r]:
+                w4.quant_act(a, a8=a8, s_a=s_a)
             if record is not None:
                 record[r][0].record(stream_ptr)
-            w4.gemm(a8, s_a, copy[(layer, g)], n, k, g, y=y, workspace=ws)
+            if fused[r]:
+                w4.linear(a, copy[(layer, g)], n, k, g, y=y, a8=a8, s_a=s_a, workspace=ws)
+            else:
+                w4.gemm(a8, s_a, copy[(layer, g)], n, k, g, y=y, workspace=ws)
             if record is not None:
                 record[r][1].record(stream_ptr)
 
@@ -295,19 +305,23 @@ def main():
     mean_us = gemm_us.mean(axis=0)
     step_bytes = sum(algo_bytes(m, n, k, g) + quant_bytes(m, k) for (m, _, n, k, g, _) in runs)
     step_ops = sum(2.0 * m * n * k for (m, _, n, k, g, _) in runs)
-    gemm_bytes = np.array([algo_bytes(m, n, k, g) for (m, _, n, k, g, _) in runs])
+    # bytes of the timed launch: a fused launch also reads A as fp16 and
+    # writes A8 and s_a instead of reading A8 and s_a (2MK more)
+    gemm_bytes = np.array([algo_bytes(m, n, k, g) + (2 * m * k if fused[r] else 0)
+                           for r, (m, _, n, k, g, _) in enumerate(runs)])
     gemm_ops = np.array([2.0 * m * n * k for (m, _, n, k, g, _) in runs])
     table = []
     for r, (m, layer, n, k, g, _) in enumerate(runs):
         t = med_us[r] * 1e-6
-        table.append({"m": m, "layer": layer, "n": n, "k": k, "g": g,
+        table.append({"m": m, "layer": layer, "n": n, "k": k, "g": g, "fused": fused[r],
                       "gemm_us_median": round(float(med_us[r]), 3),
                       "gemm_us_mean": round(float(mean_us[r]), 3),
                       "GBps": round(gemm_bytes[r] / t / 1e9, 1),
                       "TOPS": round(gemm_ops[r] / t / 1e12, 2),
                       "frac_hbm": round(gemm_bytes[r] / t / 1e9 / HBM_PEAK_GBS, 3),
                       "frac_mfma": round(gemm_ops[r] / t / 1e12 / INT8_PEAK_TOPS, 4)})
-        log(f"{layer:8s} m={m:5d} n={n:6d} k={k:6d} g={g:4d}  gemm {med_us[r]:8.2f} us  "
+        log(f"{layer:8s} m={m:5d} n={n:6d} k={k:6d} g={g:4d}  {'fused' if fused[r] else 'gemm '}"
+            f" {med_us[r]:8.2f} us  "
             f"{table[-1]['GBps']:8.1f} GB/s ({table[-1]['frac_hbm']:.3f} HBM)  "
             f"{table[-1]['TOPS']:8.1f} TOPS ({table[-1]['frac_mfma']:.3f} MFMA)")
     if args.runs_json:
@@ -348,7 +362,9 @@ def main():
         "config": {
             "workload": args.workload,
             "runs": [f"M={m} {layer} N={n} K={k} g={g}" for (m, layer, n, k, g, _) in runs],
-            "step": "w4a8_quant_act + w4a8_gemm for every run",
+            "step": "every run: w4a8_linear fused (one launch) where it applies, "
+                    "else w4a8_quant_act + w4a8_gemm",
+            "fused_runs": int(sum(fused)),
             "weight_rotation_copies": ncopies,
             "launch": "host-enqueued behind a GPU spin, events around every GEMM",
             "parallelism": "single GPU",

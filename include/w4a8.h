@@ -141,7 +141,8 @@ w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
  * m == 0 is a no-op.  Errors: INVALID_ARGUMENT, UNSUPPORTED (k % 128, n % 16,
  * k > W4A8_K_MAX, bad g), BUFFER_TOO_SMALL, DEVICE. */
 typedef struct {
-  int variant;   /* 0 auto, 1 skinny (intra-workgroup split-K), 2 tiled */
+  int variant;   /* 0 auto, 1 skinny (intra-workgroup split-K), 2 tiled;
+                    w4a8_linear only: 3 fused quantization + skinny */
   int k_split;   /* skinny: waves that split K inside a workgroup (1..8);
                     tiled: wave groups that split the k-blocks inside a
                     workgroup (1, or 2 with m_tiles 4 or 8, 2 stages);
@@ -167,6 +168,36 @@ w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
                       uint16_t* y_dev, int ldy, int32_t* acc_dev, int ldacc,
                       void* workspace_dev, size_t workspace_bytes,
                       const w4a8_gemm_opts* opts, void* stream);
+
+/* ------------------------------------------------------------ whole layer
+ * The W4A8 linear layer from fp16 activations: per-token quantization of A
+ * (as w4a8_quant_act) followed by the GEMM (as w4a8_gemm), with A8 and s_a
+ * written to a8_dev / s_a_dev as well.  For 1 or 2 tokens both steps run
+ * in one kernel: every workgroup quantizes the rows itself while its first
+ * weight loads are in flight, which saves a launch and a round trip of A8
+ * through memory; otherwise it makes the two calls in order on `stream`.
+ * (opts->variant = 3 forces the fused kernel for up to 8 tokens, when each
+ * workgroup's int8 copy of its rows fits in 96 KiB of LDS.)
+ * Outputs are bit-identical either way (Y to the last bit: the same int32
+ * sums, scales and epilogue).
+ *   a_dev     m x k fp16, row stride lda elements (lda >= k, lda % 8 == 0,
+ *             16-byte aligned)
+ *   a8_dev, s_a_dev   outputs, as w4a8_quant_act (lda8 >= k, lda8 % 16 == 0,
+ *             16-byte aligned)
+ *   other arguments as w4a8_gemm; opts->variant may also be 3 to force the
+ *   fused kernel (UNSUPPORTED where it does not apply); the workspace is the
+ *   one w4a8_gemm_workspace_size gives for the same arguments.
+ * m == 0 is a no-op.  Errors as w4a8_gemm. */
+w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
+                        const void* blob_dev, int n, int g, uint16_t* y_dev, int ldy,
+                        int8_t* a8_dev, int lda8, uint16_t* s_a_dev,
+                        int32_t* acc_dev, int ldacc, void* workspace_dev,
+                        size_t workspace_bytes, const w4a8_gemm_opts* opts, void* stream);
+
+/* Kernel launches w4a8_linear makes for these arguments: 1 (fused), 2
+ * (quantizer + GEMM) or 3 (quantizer + GEMM split over K + reduction); 0 if
+ * the call would be rejected.  Host only, no HIP call. */
+int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_opts* opts);
 
 #ifdef __cplusplus
 }

@@ -248,3 +248,53 @@ def test_gemm_workspace_size():
     assert L.w4a8_gemm_workspace_size(100, 256, 4096, 128, ctypes.byref(opts)) == 0
     assert L.w4a8_gemm_workspace_size(256, 4096, 14336, 96, None) == 0     # unsupported g
     assert L.w4a8_gemm_workspace_size(0, 4096, 14336, 128, None) == 0
+
+
+def test_linear_validates_before_any_hip_call():
+    L = w4.lib
+    fake = ctypes.c_void_p(4096)
+    # (a, lda, m, k, blob, n, g, y, ldy, a8, lda8, s_a, acc, ldacc, ws, ws_bytes, opts, stream)
+    args = [fake, 512, 4, 512, fake, 256, 128, fake, 256, fake, 512, fake, None, 0, None, 0,
+            None, None]
+    names = ["a", "lda", "m", "k", "blob", "n", "g", "y", "ldy", "a8", "lda8", "s_a", "acc",
+             "ldacc", "ws", "wsb", "opts", "stream"]
+
+    def call(**kw):
+        a = list(args)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return L.w4a8_linear(*a)
+
+    assert call(n=250) == 2
+    assert call(g=96) == 2
+    assert call(m=-1) == 1
+    assert call(m=0, a=None, a8=None, s_a=None, y=None, blob=None) == 0
+    for key in ("a", "blob", "y", "a8", "s_a"):
+        assert call(**{key: None}) == 1, key
+    assert call(lda=500) == 1                          # lda < k
+    assert call(lda=516) == 1                          # lda % 8
+    assert call(lda8=520) == 1                         # lda8 % 16
+    assert call(a=ctypes.c_void_p(4104)) == 1          # misaligned activations
+    assert call(a8=ctypes.c_void_p(4104)) == 1         # misaligned A8
+    opts = w4.GemmOpts(4)
+    assert call(opts=ctypes.byref(opts)) == 1          # no such variant
+    opts = w4.GemmOpts(3)
+    assert call(m=9, opts=ctypes.byref(opts)) == 2     # fused: at most 8 rows
+    assert call(m=4, k=131072, lda=131072, lda8=131072, opts=ctypes.byref(opts)) == 2  # long K
+
+
+def test_linear_launch_plan():
+    """w4a8_linear_launches: one fused launch for 1-2 tokens (LDS permitting),
+    two otherwise, three when the GEMM splits K over workgroups."""
+    L = w4.lib
+    assert L.w4a8_linear_launches(1, 4096, 4096, 128, None) == 1
+    assert L.w4a8_linear_launches(2, 28672, 4096, 32, None) == 1
+    assert L.w4a8_linear_launches(1, 4096, 14336, 0, None) == 1
+    assert L.w4a8_linear_launches(3, 4096, 4096, 128, None) == 2
+    assert L.w4a8_linear_launches(16, 4096, 14336, 128, None) == 2
+    assert L.w4a8_linear_launches(256, 4096, 14336, 128, None) == 3
+    assert L.w4a8_linear_launches(1, 4096, 131072, 128, None) == 2    # K range too long to fuse
+    opts = w4.GemmOpts(3)
+    assert L.w4a8_linear_launches(8, 4096, 4096, 128, ctypes.byref(opts)) == 1
+    assert L.w4a8_linear_launches(9, 4096, 4096, 128, ctypes.byref(opts)) == 0
+    assert L.w4a8_linear_launches(1, 4008, 4096, 128, None) == 0      # n % 16

@@ -74,6 +74,8 @@ def _load():
         "w4a8_quant_act": (I, [P, I, I, I, P, I, P, P]),
         "w4a8_gemm_workspace_size": (Z, [I, I, I, I, P]),
         "w4a8_gemm": (I, [P, I, P, I, P, I, I, I, P, I, P, I, P, Z, P, P]),
+        "w4a8_linear": (I, [P, I, I, I, P, I, I, P, I, P, I, P, P, I, P, Z, P, P]),
+        "w4a8_linear_launches": (I, [I, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -199,3 +201,39 @@ def gemm(a8, s_a, blob_dev, n: int, k: int, g: int, y=None, acc=None, want_acc=F
                        ctypes.byref(opts) if opts is not None else None, _stream_ptr(stream))
     _check(st, "w4a8_gemm")
     return (y, acc) if acc is not None else y
+
+
+def linear(a, blob_dev, n: int, k: int, g: int, y=None, a8=None, s_a=None, acc=None,
+           want_acc=False, variant: int = 0, k_split: int = 0, n_tiles: int = 0,
+           m_tiles: int = 0, stages: int = 0, row_groups: int = 0, slices: int = 0,
+           workspace=None, stream=None):
+    """The whole layer from fp16 activations (fused for small M); returns
+    (y, a8, s_a) or (y, a8, s_a, acc)."""
+    torch = _torch()
+    assert a.dtype == torch.float16 and a.is_cuda and a.dim() == 2 and a.stride(1) == 1
+    m = a.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=a.device)
+    if a8 is None:
+        a8 = torch.empty((m, k), dtype=torch.int8, device=a.device)
+    if s_a is None:
+        s_a = torch.empty((m,), dtype=torch.float16, device=a.device)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=a.device)
+    opts = None
+    if variant or k_split or n_tiles or m_tiles or stages or row_groups or slices:
+        opts = GemmOpts(variant, k_split, n_tiles, m_tiles, stages, row_groups, slices)
+    ws_opts = opts if (opts is None or variant != 3) else None
+    ws_need = 0 if variant == 3 else int(lib.w4a8_gemm_workspace_size(
+        m, n, k, g, ctypes.byref(ws_opts) if ws_opts is not None else None))
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=a.device)
+    st = lib.w4a8_linear(a.data_ptr(), a.stride(0), m, k, blob_dev.data_ptr(), n, g,
+                         y.data_ptr(), y.stride(0), a8.data_ptr(), a8.stride(0), s_a.data_ptr(),
+                         acc.data_ptr() if acc is not None else None,
+                         acc.stride(0) if acc is not None else 0,
+                         workspace.data_ptr() if workspace is not None else None,
+                         workspace.numel() if workspace is not None else 0,
+                         ctypes.byref(opts) if opts is not None else None, _stream_ptr(stream))
+    _check(st, "w4a8_linear")
+    return (y, a8, s_a, acc) if acc is not None else (y, a8, s_a)

@@ -218,6 +218,8 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
   p.ldacc = acc_dev ? ldacc : 0;
   p.part = nullptr;
   p.kb_per_slice = k / kKBlock;
+  p.a8_out = nullptr;
+  p.s_a_out = nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -232,6 +234,91 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
     if (e == hipSuccess && pl.slices > 1) e = launch_split_reduce(p, pl.slices, s);
   }
   return device_status(e);
+}
+
+namespace {
+
+// Skinny configuration for the fused kernel: the automatic skinny choice
+// with one row tile, at most 2 column tiles per wave above 4 rows, and each
+// wave's K range at most 16 blocks; forced options as for w4a8_gemm.
+SkinnyConfig fused_plan(int m, int n, int k, const w4a8_gemm_opts* opts) {
+  SkinnyConfig c = choose_skinny(m, n, k);
+  c.mr = 1;
+  if (m > 4 && c.nc > 2) {
+    c.nc = 2;
+    c.kw = std::min(8, std::max(1, (k / kKBlock) / 4));
+    c.kbw = blocks_per_wave(k / kKBlock, c.kw);
+    c.kw = (k / kKBlock + c.kbw - 1) / c.kbw;
+  }
+  if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
+  if (opts && opts->k_split > 0) {
+    c.kw = opts->k_split;
+    c.kbw = blocks_per_wave(k / kKBlock, c.kw);
+  }
+  return c;
+}
+
+}  // namespace
+
+extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
+                                   const void* blob_dev, int n, int g, uint16_t* y_dev, int ldy,
+                                   int8_t* a8_dev, int lda8, uint16_t* s_a_dev, int32_t* acc_dev,
+                                   int ldacc, void* workspace_dev, size_t workspace_bytes,
+                                   const w4a8_gemm_opts* opts, void* stream) {
+  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
+  if (m == 0) return W4A8_OK;
+  if (!a_dev || !blob_dev || !y_dev || !a8_dev || !s_a_dev) return W4A8_ERR_INVALID_ARGUMENT;
+  if (lda < k || lda % 8 || lda8 < k || lda8 % 16 || ldy < n || (acc_dev && ldacc < n))
+    return W4A8_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a_dev) || !aligned16(a8_dev) || !aligned16(blob_dev))
+    return W4A8_ERR_INVALID_ARGUMENT;
+  const int variant = opts ? opts->variant : 0;
+  if (variant < 0 || variant > 3) return W4A8_ERR_INVALID_ARGUMENT;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const SkinnyConfig fc = fused_plan(m, n, k, opts);
+  const bool fused_ok = fused_config_supported(fc, m, k);
+  if (variant == 3 && !fused_ok) return W4A8_ERR_UNSUPPORTED;
+  if (variant == 3 || (variant == 0 && fused_ok && m <= kFusedAutoRows)) {
+    Sections sec = sections(n, k, g);
+    const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
+    GemmParams p{};
+    p.a8 = a8_dev;
+    p.lda8 = lda8;
+    p.s_a = s_a_dev;
+    p.m = m;
+    p.q = base + sec.q_off;
+    p.meta = base + sec.meta_off;
+    p.s1 = reinterpret_cast<const uint16_t*>(base + sec.s1_off);
+    p.n = n;
+    p.k = k;
+    p.meta_row_bytes = sec.meta_row_bytes;
+    p.y = y_dev;
+    p.ldy = ldy;
+    p.acc = acc_dev;
+    p.ldacc = acc_dev ? ldacc : 0;
+    p.part = nullptr;
+    p.kb_per_slice = k / kKBlock;
+    p.a8_out = a8_dev;
+    p.s_a_out = s_a_dev;
+    return device_status(launch_gemm_fused(p, a_dev, lda, groups_per_block(k, g), fc, s));
+  }
+  // two launches: the quantizer, then the GEMM on its output
+  w4a8_status st = w4a8_quant_act(a_dev, m, k, lda, a8_dev, lda8, s_a_dev, stream);
+  if (st != W4A8_OK) return st;
+  return w4a8_gemm(a8_dev, lda8, s_a_dev, m, blob_dev, n, k, g, y_dev, ldy, acc_dev, ldacc,
+                   workspace_dev, workspace_bytes, opts, stream);
+}
+
+extern "C" int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_opts* opts) {
+  if (m <= 0 || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
+  const int variant = opts ? opts->variant : 0;
+  if (variant < 0 || variant > 3) return 0;
+  const bool fused_ok = fused_config_supported(fused_plan(m, n, k, opts), m, k);
+  if (variant == 3) return fused_ok ? 1 : 0;
+  if (variant == 0 && fused_ok && m <= kFusedAutoRows) return 1;
+  return plan_gemm(m, n, k, opts).slices > 1 ? 3 : 2;
 }
 
 extern "C" const char* w4a8_last_device_error(void) {

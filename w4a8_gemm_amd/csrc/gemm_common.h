@@ -27,6 +27,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "quant_common.h"
 
 namespace w4a8 {
 namespace dev {
@@ -69,14 +70,6 @@ __device__ __forceinline__ v4i decode16(uint32_t w0, uint32_t w1, GroupConst g) 
   b[2] = int(dec4(w1 & 0x0F0F0F0Fu, g));
   b[3] = int(dec4((w1 >> 4) & 0x0F0F0F0Fu, g));
   return b;
-}
-
-__device__ __forceinline__ uint16_t f2h_bits(float v) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-}
-
-__device__ __forceinline__ float h2f(uint16_t h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
 // Epilogue scales of one lane, fetched at kernel start so that the final

@@ -23,6 +23,8 @@ struct GemmParams {
   int kb_per_wave;       // skinny: 128-k blocks per wave (a multiple of 4 / groups-per-block)
   int32_t* part;         // tiled, K split over workgroups: slices x m x n int32 partial sums
   int kb_per_slice;      // tiled: 128-k blocks per K slice (all of K when not split)
+  int8_t* a8_out;        // fused: A8 written by workgroup 0 (row stride lda8)
+  uint16_t* s_a_out;     // fused: s_a written by workgroup 0
 };
 
 constexpr int kMaxSlices = 16;   // workgroups splitting K of one tile
@@ -60,6 +62,18 @@ hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
                              hipStream_t stream);
 hipError_t launch_split_reduce(const GemmParams& p, int slices, hipStream_t stream);
 bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb);
+
+// Fused quantization + skinny GEMM: M <= kFusedMaxRows, one row tile, each
+// wave's K range at most 16 blocks, LDS within kFusedMaxLds.  The automatic
+// choice takes it up to kFusedAutoRows tokens: beyond that the per-workgroup
+// quantization costs more than the launch it saves (timed on MI355X over the
+// Llama-3-8B decode layers: M = 1 gains 1.6-3 us per layer, M = 4 loses).
+constexpr int kFusedMaxRows = 8;
+constexpr int kFusedAutoRows = 2;
+constexpr size_t kFusedMaxLds = 96 * 1024;
+bool fused_config_supported(const SkinnyConfig& c, int m, int k);
+hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, int gpb,
+                             const SkinnyConfig& c, hipStream_t stream);
 bool tiled_config_supported(const TiledConfig& c);
 
 }  // namespace w4a8
