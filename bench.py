@@ -168,7 +168,8 @@ def main():
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
     if args.print_source_hash:
-        for files in (["skinny.hip", "gemm_common.h"], ["tiled.hip", "gemm_common.h"]):
+        for files in (["skinny.hip", "gemm_common.h", "quant_common.h"],
+                      ["tiled.hip", "gemm_common.h", "quant_common.h"]):
             print(" + ".join(files), source_hash(files))
         return
 
