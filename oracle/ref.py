@@ -24,6 +24,7 @@ steps below are the plainest reading of that description:
   O3  per-token symmetric int8 activations with an fp16 scale s_a[m]
       (per-token dynamic quantization is the usual practice the PrefixQuant
       page contrasts against, section "Key Findings")
+  O3' the static alternative: one fp16 scale for the whole tensor
   O4  acc[m, n] = sum_k A8[m, k] * W8^[n, k]   (exact integer)
   O5  Y[m, n]   = fp16(acc * s_a[m] * s1[n])   (the scale epilogue)
 
@@ -185,6 +186,24 @@ def quant_act(a: np.ndarray):
     s_a = to_f16(alpha / F32(A8_LIMIT))
     r = _safe_recip(s_a)
     a8 = np.clip(np.rint(a32 * r[:, None]), -A8_LIMIT, A8_LIMIT)
+    return a8.astype(np.int8), s_a
+
+
+def quant_act_static(a: np.ndarray, scale_f16) -> tuple:
+    """O3' (static per-tensor activation scale): one fp16 scale s fixed
+    ahead of time for the whole tensor, so no per-token reduction runs (the
+    static alternative the PrefixQuant page sets against per-token dynamic
+    quantization, section "Key Findings").
+
+    A8 = clamp(rint(fp32(A * fp32(1/s))), -127, 127), and 0 where s = 0;
+    s_a[m] = s for every row, so the GEMM epilogue is unchanged.
+    Returns (A8 int8[M, K], s_a float16[M]).
+    """
+    a32 = np.asarray(a, dtype=np.float16).astype(F32)
+    s = to_f16(np.asarray(scale_f16, dtype=np.float16).reshape(()))
+    r = _safe_recip(s.reshape(1))[0]
+    a8 = np.clip(np.rint(a32 * r), -A8_LIMIT, A8_LIMIT)
+    s_a = np.full(a32.shape[0], s, dtype=np.float16)
     return a8.astype(np.int8), s_a
 
 

@@ -456,3 +456,82 @@ def test_gemm_pins_catch_mutants():
 
     assert not gemm_brute_check(transposed_k)
     assert not gemm_brute_check(int16_wrap)
+
+
+# ------------------------------------------------------------ O3' static scale
+def _rne_fraction(x: Fraction) -> int:
+    f = x.numerator // x.denominator
+    r = x - f
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return f
+
+
+def act_static_golden_check(fn):
+    """Hand-worked cases (tests/golden/act_static_cases.txt); returns mismatches."""
+    bad = []
+    with open(os.path.join(GOLDEN, "act_static_cases.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            sc, av, ex = (x.strip() for x in line.split("|"))
+            a = np.array([[float(v) for v in av.split()]], dtype=np.float16)
+            want = np.array([[int(v) for v in ex.split()]], dtype=np.int8)
+            a8, s_a = fn(a, np.float16(float(sc)))
+            if not np.array_equal(a8, want) or s_a[0] != np.float16(float(sc)):
+                bad.append(line.strip())
+    return bad
+
+
+def act_static_exhaustive_check(fn, exponents=(-14, -3, 0, 5)):
+    """Every finite fp16 input at power-of-two scales, where A * (1/s) is exact:
+    the result must be the exact rational A / s rounded half-to-even and
+    clamped to +-127.  Returns the number of mismatches."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    vals = vals[np.isfinite(vals)]
+    bad = 0
+    for e in exponents:
+        s = np.float16(2.0 ** e)
+        a8, _ = fn(vals[None, :], s)
+        want = np.array([max(-127, min(127, _rne_fraction(Fraction(float(v)) / Fraction(2) ** e)))
+                         for v in vals], dtype=np.int64)
+        bad += int(np.sum(a8[0].astype(np.int64) != want))
+    return bad
+
+
+def test_act_static_golden():
+    assert act_static_golden_check(ref.quant_act_static) == []
+
+
+def test_act_static_exhaustive_power_of_two_scales():
+    assert act_static_exhaustive_check(ref.quant_act_static) == 0
+
+
+def test_act_static_invariants():
+    a = synth.activations(7, 300, seed=41)
+    for s in (np.float16(0.01), np.float16(0.3), np.float16(7.0)):
+        a8, s_a = ref.quant_act_static(a, s)
+        assert (s_a == s).all() and s_a.dtype == np.float16
+        assert np.abs(a8.astype(np.int64)).max() <= 127
+        nz = a8 != 0
+        assert (np.sign(a8[nz]) == np.sign(a[nz].astype(np.float32))).all()
+    a8, s_a = ref.quant_act_static(a, np.float16(0.0))
+    assert not a8.any() and not s_a.astype(np.float32).any()
+
+
+def test_act_static_pins_catch_mutants():
+    def round_half_up(a, s):
+        a32 = np.asarray(a, np.float16).astype(np.float32)
+        r = np.float32(1) / np.float32(s) if float(s) else np.float32(0)
+        a8 = np.clip(np.floor(a32 * r + np.float32(0.5)), -127, 127).astype(np.int8)
+        return a8, np.full(a32.shape[0], s, np.float16)
+
+    def clamp_128(a, s):
+        a32 = np.asarray(a, np.float16).astype(np.float32)
+        r = np.float32(1) / np.float32(s) if float(s) else np.float32(0)
+        a8 = np.clip(np.rint(a32 * r), -128, 127).astype(np.int8)
+        return a8, np.full(a32.shape[0], s, np.float16)
+
+    for mutant in (round_half_up, clamp_128):
+        assert act_static_golden_check(mutant) or act_static_exhaustive_check(mutant, (0,)) > 0
