@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--runs-json", default="")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step (reported as context)")
+    ap.add_argument("--static-scale", type=float, default=None,
+                    help="quantize activations with this one static fp16 scale "
+                         "(w4a8_quant_act_static) instead of per-token scales")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
@@ -230,12 +233,14 @@ def main():
     # small M: quantization fused into the GEMM (one launch, w4a8_linear);
     # else the quantizer, then the GEMM; events bracket the GEMM launch
     fused = [int(w4.lib.w4a8_linear_launches(m, n, k, g, None)) == 1
-             for (m, _, n, k, g, _) in runs]
+             and args.static_scale is None for (m, _, n, k, g, _) in runs]
 
     def launch_step(copy, record=None):
         for r, (m, layer, n, k, g, _) in enumerate(runs):
             a, a8, s_a, y, ws = bufs[r]
-            if not fused[r]:
+            if args.static_scale is not None:
+                w4.quant_act_static(a, args.static_scale, a8=a8, s_a=s_a)
+            elif not fused[r]:
                 w4.quant_act(a, a8=a8, s_a=s_a)
             if record is not None:
                 record[r][0].record(stream_ptr)
@@ -366,6 +371,8 @@ def main():
             "step": "every run: w4a8_linear fused (one launch) where it applies, "
                     "else w4a8_quant_act + w4a8_gemm",
             "fused_runs": int(sum(fused)),
+            "activation_scale": ("static per-tensor %g" % args.static_scale
+                                 if args.static_scale is not None else "per-token dynamic"),
             "weight_rotation_copies": ncopies,
             "launch": "host-enqueued behind a GPU spin, events around every GEMM",
             "parallelism": "single GPU",

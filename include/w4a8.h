@@ -120,6 +120,18 @@ w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
                            int8_t* a8_dev, int lda8, uint16_t* s_a_dev,
                            void* stream);
 
+/* Static per-tensor variant (the static alternative to per-token scaling on
+ * the PrefixQuant page, "Key Findings"): one fp16 scale for the whole tensor,
+ * fixed ahead of time, so no reduction runs.
+ *   A8 = clamp(rint(A * fp32(1 / scale)), +-127)  (0 when scale == 0)
+ *   s_a_dev[m] = scale for every row, so w4a8_gemm consumes it unchanged.
+ * scale_f16 is the fp16 bit pattern of a finite value >= 0.  Layouts as for
+ * w4a8_quant_act.  Errors: INVALID_ARGUMENT (as w4a8_quant_act, or a negative,
+ * infinite or NaN scale), DEVICE. */
+w4a8_status w4a8_quant_act_static(const uint16_t* a_dev, int m, int k, int lda,
+                                  uint16_t scale_f16, int8_t* a8_dev, int lda8,
+                                  uint16_t* s_a_dev, void* stream);
+
 /* -------------------------------------------------------------- W4A8 GEMM
  * Y = fp16(s_a[m] * s1[n] * sum_k A8[m,k] * W8^[n,k]) with int32 accumulation.
  *   a8_dev    m x k int8, row stride lda8 bytes (lda8 >= k, lda8 % 16 == 0,

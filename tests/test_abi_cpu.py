@@ -177,6 +177,13 @@ def test_gpu_entry_points_validate_before_any_hip_call():
     assert L.w4a8_quant_act(fake, 4, 8, 7, fake, 8, fake, None) == 1      # lda < k
     assert L.w4a8_quant_act(None, 4, 8, 8, fake, 8, fake, None) == 1      # null
     assert L.w4a8_quant_act(None, 0, 8, 8, None, 8, None, None) == 0      # m == 0: no-op
+    # static scale: finite and >= 0 (fp16 bits), else rejected
+    one = 0x3C00
+    for bad in (0xBC00, 0x7C00, 0xFC00, 0x7E00, 0x8001):              # -1, +inf, -inf, NaN, -tiny
+        assert L.w4a8_quant_act_static(fake, 4, 8, 8, bad, fake, 8, fake, None) == 1, hex(bad)
+    assert L.w4a8_quant_act_static(fake, 4, 8, 7, one, fake, 8, fake, None) == 1  # lda < k
+    assert L.w4a8_quant_act_static(fake, 4, 8, 8, one, None, 8, fake, None) == 1  # null
+    assert L.w4a8_quant_act_static(None, 0, 8, 8, one, None, 8, None, None) == 0  # m == 0
     # gemm: (a8, lda8, s_a, m, blob, n, k, g, y, ldy, acc, ldacc, ws, ws_bytes, opts, stream)
     args = [fake, 512, fake, 4, fake, 256, 512, 128, fake, 256, None, 0, None, 0, None, None]
 

@@ -71,6 +71,44 @@ def test_quant_act_strided_rows():
     assert np.array_equal(s_a.cpu().numpy().view(np.uint16), want_sa.view(np.uint16))
 
 
+@pytest.mark.parametrize("scale", [0.0, 6e-08, 0.001, 0.05, 3.0, 1000.0])
+@pytest.mark.parametrize("m,k", [(1, 4096), (16, 14336), (37, 1000), (3, 7), (5, 8), (2, 24576)])
+def test_quant_act_static_bit_exact(m, k, scale):
+    """Static per-tensor scale: A8 and s_a bit-exact with the oracle, on the
+    vector and the scalar path, with scales that clamp everything, nothing,
+    or flush everything to 0."""
+    import torch
+    dev = device()
+    a = synth.activations(m, k, seed=m * 7 + k)
+    s = np.float16(scale)
+    log(f"quant_act_static m={m} k={k} scale={float(s)!r}")
+    a8, s_a = w4.quant_act_static(torch.from_numpy(a).to(dev), float(s))
+    torch.cuda.synchronize()
+    want_a8, want_sa = ref.quant_act_static(a, s)
+    assert np.array_equal(s_a.cpu().numpy().view(np.uint16), want_sa.view(np.uint16))
+    assert np.array_equal(a8.cpu().numpy(), want_a8)
+
+
+def test_quant_act_static_then_gemm():
+    """The GEMM consumes the static scales unchanged."""
+    m, n, k, g = 24, 272, 1152, 64
+    w = synth.weights(n, k, seed=31, dist="student_t4")
+    a = synth.activations(m, k, seed=32)
+    s = np.float16(0.125)
+    qw = ref.quantize_weights(w, g)
+    want_a8, want_sa = ref.quant_act_static(a, s)
+    acc_ref = ref.gemm_acc(want_a8, ref.decoded_weights(qw))
+    y_ref = ref.epilogue(acc_ref, want_sa, qw["s1"])
+    import torch
+    dev = device()
+    log("quant_act_static + gemm")
+    a8, s_a = w4.quant_act_static(torch.from_numpy(a).to(dev), float(s))
+    y, acc = w4.gemm(a8, s_a, w4.to_device(w4.pack(w, g), dev), n, k, g, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert ref.y_tolerance_ok(y.cpu().numpy(), y_ref).all()
+
+
 # ------------------------------------------------------------ GEMM, whole outputs
 SMALL = [
     # m, n, k, g, dist

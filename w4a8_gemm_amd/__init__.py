@@ -72,6 +72,7 @@ def _load():
         "w4a8_blob_info": (I, [P, Z, P, P, P]),
         "w4a8_unpack": (I, [P, Z, P, P, P, P]),
         "w4a8_quant_act": (I, [P, I, I, I, P, I, P, P]),
+        "w4a8_quant_act_static": (I, [P, I, I, I, ctypes.c_uint16, P, I, P, P]),
         "w4a8_gemm_workspace_size": (Z, [I, I, I, I, P]),
         "w4a8_gemm": (I, [P, I, P, I, P, I, I, I, P, I, P, I, P, Z, P, P]),
         "w4a8_linear": (I, [P, I, I, I, P, I, I, P, I, P, I, P, P, I, P, Z, P, P]),
@@ -171,6 +172,24 @@ def quant_act(a, a8=None, s_a=None, stream=None):
         s_a = torch.empty((m,), dtype=torch.float16, device=a.device)
     _check(lib.w4a8_quant_act(a.data_ptr(), m, k, a.stride(0), a8.data_ptr(), a8.stride(0),
                               s_a.data_ptr(), _stream_ptr(stream)), "w4a8_quant_act")
+    return a8, s_a
+
+
+def quant_act_static(a, scale, a8=None, s_a=None, stream=None):
+    """Int8 quantization of an M x K float16 CUDA tensor with one static
+    fp16 scale; s_a is filled with the scale for every row."""
+    import numpy as np
+    torch = _torch()
+    assert a.dtype == torch.float16 and a.is_cuda and a.dim() == 2 and a.stride(1) == 1
+    m, k = a.shape
+    if a8 is None:
+        a8 = torch.empty((m, k), dtype=torch.int8, device=a.device)
+    if s_a is None:
+        s_a = torch.empty((m,), dtype=torch.float16, device=a.device)
+    bits = int(np.array([scale], dtype=np.float16).view(np.uint16)[0])
+    _check(lib.w4a8_quant_act_static(a.data_ptr(), m, k, a.stride(0), bits, a8.data_ptr(),
+                                     a8.stride(0), s_a.data_ptr(), _stream_ptr(stream)),
+           "w4a8_quant_act_static")
     return a8, s_a
 
 

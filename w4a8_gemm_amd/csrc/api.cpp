@@ -56,7 +56,10 @@ SkinnyConfig choose_skinny(int m, int n, int k) {
   }
   kw = std::min(kw, std::max(1, kblocks / 4));
   c.kbw = blocks_per_wave(kblocks, kw);
-  c.kw = (kblocks + c.kbw - 1) / c.kbw;
+  // keep all kw waves even when rounding the range up to a multiple of 4
+  // blocks leaves the last one idle: two waves on every SIMD beat an uneven
+  // split (K = 14336: 8 waves with one idle are 5 % faster than 7)
+  c.kw = kw;
   return c;
 }
 
@@ -84,6 +87,19 @@ extern "C" w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int l
   if (!a_dev || !a8_dev || !s_a_dev) return W4A8_ERR_INVALID_ARGUMENT;
   return device_status(launch_quant_act(a_dev, m, k, lda, a8_dev, lda8, s_a_dev,
                                         static_cast<hipStream_t>(stream)));
+}
+
+extern "C" w4a8_status w4a8_quant_act_static(const uint16_t* a_dev, int m, int k, int lda,
+                                             uint16_t scale_f16, int8_t* a8_dev, int lda8,
+                                             uint16_t* s_a_dev, void* stream) {
+  if (m < 0 || k <= 0 || lda < k || lda8 < k) return W4A8_ERR_INVALID_ARGUMENT;
+  // the scale must be a finite, non-negative fp16 value (sign bit clear,
+  // exponent field not all ones)
+  if ((scale_f16 & 0x8000u) || (scale_f16 & 0x7C00u) == 0x7C00u) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m == 0) return W4A8_OK;
+  if (!a_dev || !a8_dev || !s_a_dev) return W4A8_ERR_INVALID_ARGUMENT;
+  return device_status(launch_quant_act_static(a_dev, m, k, lda, scale_f16, a8_dev, lda8, s_a_dev,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 namespace {

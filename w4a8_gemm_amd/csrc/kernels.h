@@ -53,6 +53,8 @@ struct TiledConfig {
 
 hipError_t launch_quant_act(const uint16_t* a, int m, int k, int lda, int8_t* a8, int lda8,
                             uint16_t* s_a, hipStream_t stream);
+hipError_t launch_quant_act_static(const uint16_t* a, int m, int k, int lda, uint16_t scale_bits,
+                                   int8_t* a8, int lda8, uint16_t* s_a, hipStream_t stream);
 hipError_t launch_gemm_skinny(const GemmParams& p, int gpb, const SkinnyConfig& c,
                               hipStream_t stream);
 // slices > 1: workgroup (tile, slice) covers k-blocks [slice * kb_per_slice,

@@ -87,7 +87,44 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t* __r
   }
 }
 
+// Static per-tensor scale: no reduction, each thread quantizes 8 halves (or
+// one when rows are not 16-byte aligned) with the multiplier fp32(1 / s)
+// and row 0's threads also write s_a[m] = s for the GEMM epilogue.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_act_static_kernel(
+    const uint16_t* __restrict__ a, int m, int k, int lda, uint16_t scale_bits,
+    int8_t* __restrict__ a8, int lda8, uint16_t* __restrict__ s_a) {
+  const float r = act_recip(scale_bits);
+  const int per = VEC ? 8 : 1;
+  const int row_items = (k + per - 1) / per;
+  const long idx = long(blockIdx.x) * kThreads + threadIdx.x;
+  if (idx < m) s_a[idx] = scale_bits;
+  if (idx >= long(m) * row_items) return;
+  const int row = int(idx / row_items);
+  const int i = int(idx - long(row) * row_items) * per;
+  const uint16_t* src = a + size_t(row) * size_t(lda) + i;
+  int8_t* dst = a8 + size_t(row) * size_t(lda8) + i;
+  if (VEC)
+    *reinterpret_cast<uint2*>(dst) = quant8(*reinterpret_cast<const uint4*>(src), r);
+  else
+    *dst = int8_t(quant1(*src, r));
+}
+
 }  // namespace
+
+hipError_t launch_quant_act_static(const uint16_t* a, int m, int k, int lda, uint16_t scale_bits,
+                                   int8_t* a8, int lda8, uint16_t* s_a, hipStream_t stream) {
+  const bool vec = (k % 8 == 0) && (lda % 8 == 0) && (lda8 % 8 == 0) &&
+                   (reinterpret_cast<uintptr_t>(a) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(a8) % 8 == 0);
+  const long items = long(m) * (vec ? k / 8 : k);
+  const long threads = items > m ? items : m;
+  dim3 grid(unsigned((threads + kThreads - 1) / kThreads)), block(kThreads);
+  void* args[] = {&a, &m, &k, &lda, &scale_bits, &a8, &lda8, &s_a};
+  const void* fn = vec ? reinterpret_cast<const void*>(&quant_act_static_kernel<true>)
+                       : reinterpret_cast<const void*>(&quant_act_static_kernel<false>);
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
 
 hipError_t launch_quant_act(const uint16_t* a, int m, int k, int lda, int8_t* a8, int lda8,
                             uint16_t* s_a, hipStream_t stream) {
