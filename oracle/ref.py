@@ -251,6 +251,44 @@ def y_tolerance_ok(y, y_ref) -> np.ndarray:
     return diff <= 1e-3 * np.abs(y_ref.astype(np.float64)) + ulp
 
 
+# ---------------------------------------------------------------- W4A16
+# The comparison path (the W4A16 kernels the pages measure against: the
+# AWQ-style weight-only baseline of the QServe/QoQ abstract, QUICK's and
+# FLUTE's mixed-precision GEMMs): the same 4-bit weights, decoded to fp16
+# and multiplied with fp16 activations in fp32.  Reading: the fp16 weight is
+# the level-1 dequantization of the decoded int8 weight, rounded once,
+#     W16^[n, k] = fp16(s1[n] * W8^[n, k])
+# (s1 * W8^ is exact in float64), and
+#     Y16[m, n] = fp16(sum_k A[m, k] * W16^[n, k])  (exact sum, one rounding).
+def w16_weights(qw: dict) -> np.ndarray:
+    """W16^ = fp16(s1 * W8^): one rounding of the exact product."""
+    w8 = decoded_weights(qw).astype(np.float64)
+    return to_f16(qw["s1"].astype(np.float64)[:, None] * w8)
+
+
+def w4a16_linear(a: np.ndarray, qw: dict):
+    """Y16 = fp16(A @ W16^.T) with the sum taken in float64.  Returns
+    (Y16 float16[M, N], W16^ float16[N, K], sum_abs float64[M, N]) where
+    sum_abs = sum_k |A * W16^| bounds any accumulation error."""
+    w16 = w16_weights(qw).astype(np.float64)
+    a64 = np.asarray(a, dtype=np.float16).astype(np.float64)
+    y = a64 @ w16.T
+    sum_abs = np.abs(a64) @ np.abs(w16).T
+    return to_f16(y), w16.astype(np.float16), sum_abs
+
+
+def y16_tolerance_ok(y, y_ref, sum_abs, k: int) -> np.ndarray:
+    """Bar for an fp32-accumulated fp16 GEMM: one fp16 ulp at Y_ref, plus
+    1e-3 |Y_ref|, plus the first-order fp32 summation bound K * 2^-24 *
+    sum_k |A * W16^| (products of two fp16 values are exact in fp32)."""
+    y = np.asarray(y, dtype=np.float16).astype(np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float16)
+    ulp = np.spacing(np.abs(y_ref)).astype(np.float64)
+    yr = y_ref.astype(np.float64)
+    bound = ulp + 1e-3 * np.abs(yr) + k * 2.0 ** -24 * np.asarray(sum_abs, np.float64)
+    return np.abs(y - yr) <= bound
+
+
 # ---------------------------------------------------------------- whole layer
 def linear(a: np.ndarray, w: np.ndarray, g: int):
     """The whole layer on the CPU: returns every intermediate, for tests."""

@@ -535,3 +535,81 @@ def test_act_static_pins_catch_mutants():
 
     for mutant in (round_half_up, clamp_128):
         assert act_static_golden_check(mutant) or act_static_exhaustive_check(mutant, (0,)) > 0
+
+
+# ------------------------------------------------------------ W4A16 comparison path
+def w16_exact_check(fn, w, g):
+    """W16^ against the exact rational s1 * W8^ rounded half-to-even by
+    half_of_fraction (no numpy rounding involved); returns mismatches."""
+    qw = ref.quantize_weights(w, g)
+    got = fn(qw).astype(np.float64)
+    w8 = ref.decoded_weights(qw)
+    bad = 0
+    for n in range(w8.shape[0]):
+        s1 = Fraction(float(qw["s1"][n]))
+        for kk in range(w8.shape[1]):
+            if got[n, kk] != half_of_fraction(s1 * int(w8[n, kk])):
+                bad += 1
+    return bad
+
+
+def test_w16_weights_single_rounding_of_exact_product():
+    w = synth.weights(24, 256, seed=61, dist="student_t4")
+    for g in (32, 128, 0):
+        assert w16_exact_check(ref.w16_weights, w, g) == 0
+
+
+def w4a16_brute_check(fn):
+    """Y16 on a tiny case against an exact rational sum rounded once."""
+    rng = np.random.default_rng(62)
+    w = synth.weights(8, 128, seed=63)
+    a = (rng.standard_normal((3, 128)) * 2).astype(np.float16)
+    qw = ref.quantize_weights(w, 64)
+    y, w16, sum_abs = fn(a, qw)
+    bad = 0
+    for m in range(3):
+        for n in range(8):
+            exact = sum(Fraction(float(a[m, kk])) * Fraction(float(w16[n, kk])) for kk in range(128))
+            if float(y[m, n]) != half_of_fraction(exact):
+                bad += 1
+            if abs(sum_abs[m, n] - float(sum(abs(Fraction(float(a[m, kk])) * Fraction(float(w16[n, kk])))
+                                              for kk in range(128)))) > 1e-9 * max(1.0, sum_abs[m, n]):
+                bad += 1
+    return bad
+
+
+def test_w4a16_brute_force():
+    assert w4a16_brute_check(ref.w4a16_linear) == 0
+
+
+def test_w4a16_tolerance_rule():
+    y_ref = np.array([1.0, -2.0, 1000.0], np.float16)
+    s = np.array([1.0, 1.0, 1.0])
+    assert ref.y16_tolerance_ok(y_ref, y_ref, s, 4096).all()
+    # one ulp off passes; far off fails
+    assert ref.y16_tolerance_ok(np.nextafter(y_ref, np.float16(np.inf)), y_ref, s, 4096).all()
+    assert not ref.y16_tolerance_ok(y_ref * np.float16(1.01), y_ref, s, 4096).any()
+    # the accumulation term scales with K and sum |A W|
+    assert ref.y16_tolerance_ok(np.float16(1.0) + np.float16(0.03), np.float16(1.0),
+                                np.float64(2 ** 14), 2 ** 9)
+
+
+def test_w4a16_pins_catch_mutants():
+    def w16_truncating(qw):
+        w8 = ref.decoded_weights(qw).astype(np.float64)
+        v = qw["s1"].astype(np.float64)[:, None] * w8
+        # round toward zero in fp16
+        f = v.astype(np.float16)
+        over = np.abs(f.astype(np.float64)) > np.abs(v)
+        f[over] = np.nextafter(f[over], np.float16(0))
+        return f
+    w = synth.weights(24, 256, seed=61, dist="student_t4")
+    assert w16_exact_check(w16_truncating, w, 128) > 0
+
+    def y_fp16_accumulate(a, qw):               # accumulating in fp16 loses the sum
+        y, w16, sa = ref.w4a16_linear(a, qw)
+        acc = np.zeros((a.shape[0], w16.shape[0]), np.float16)
+        for kk in range(a.shape[1]):
+            acc = (acc + (a[:, kk:kk + 1].astype(np.float16) * w16[:, kk][None, :]).astype(np.float16))
+        return acc, w16, sa
+    assert w4a16_brute_check(y_fp16_accumulate) > 0
