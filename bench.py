@@ -41,6 +41,12 @@ def algo_bytes(m, n, k, g):
     return n * k / 2 + meta + 2 * n + m * k + 2 * m + 2 * m * n
 
 
+def w4a16_bytes(m, n, k, g):
+    """The W4A16 comparison GEMM: the same weight bytes, fp16 A in, fp16 Y out."""
+    meta = 0.5 * n if g in (0, k) else 1.5 * n * k / g
+    return n * k / 2 + meta + 2 * n + 2 * m * k + 2 * m * n
+
+
 def quant_bytes(m, k):
     return 3 * m * k + 2 * m
 
@@ -167,6 +173,9 @@ def main():
     ap.add_argument("--static-scale", type=float, default=None,
                     help="quantize activations with this one static fp16 scale "
                          "(w4a8_quant_act_static) instead of per-token scales")
+    ap.add_argument("--w4a16", action="store_true",
+                    help="time the W4A16 comparison GEMM (same packed weights, fp16 "
+                         "activations) in place of the W4A8 layer; M <= 64 workloads")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
@@ -233,11 +242,21 @@ def main():
     # small M: quantization fused into the GEMM (one launch, w4a8_linear);
     # else the quantizer, then the GEMM; events bracket the GEMM launch
     fused = [int(w4.lib.w4a8_linear_launches(m, n, k, g, None)) == 1
-             and args.static_scale is None for (m, _, n, k, g, _) in runs]
+             and args.static_scale is None and not args.w4a16 for (m, _, n, k, g, _) in runs]
+    if args.w4a16 and max(r[0] for r in runs) > 64:
+        print("--w4a16: the W4A16 comparison kernel covers M <= 64 only", file=sys.stderr)
+        sys.exit(2)
 
     def launch_step(copy, record=None):
         for r, (m, layer, n, k, g, _) in enumerate(runs):
             a, a8, s_a, y, ws = bufs[r]
+            if args.w4a16:
+                if record is not None:
+                    record[r][0].record(stream_ptr)
+                w4.w4a16(a, copy[(layer, g)], n, k, g, y=y)
+                if record is not None:
+                    record[r][1].record(stream_ptr)
+                continue
             if args.static_scale is not None:
                 w4.quant_act_static(a, args.static_scale, a8=a8, s_a=s_a)
             elif not fused[r]:
@@ -309,11 +328,13 @@ def main():
     gemm_us = np.array(per_step_gemm) * 1e3
     med_us = np.median(gemm_us, axis=0)
     mean_us = gemm_us.mean(axis=0)
-    step_bytes = sum(algo_bytes(m, n, k, g) + quant_bytes(m, k) for (m, _, n, k, g, _) in runs)
+    step_bytes = sum(w4a16_bytes(m, n, k, g) if args.w4a16 else
+                     algo_bytes(m, n, k, g) + quant_bytes(m, k) for (m, _, n, k, g, _) in runs)
     step_ops = sum(2.0 * m * n * k for (m, _, n, k, g, _) in runs)
     # bytes of the timed launch: a fused launch also reads A as fp16 and
     # writes A8 and s_a instead of reading A8 and s_a (2MK more)
-    gemm_bytes = np.array([algo_bytes(m, n, k, g) + (2 * m * k if fused[r] else 0)
+    gemm_bytes = np.array([w4a16_bytes(m, n, k, g) if args.w4a16 else
+                           algo_bytes(m, n, k, g) + (2 * m * k if fused[r] else 0)
                            for r, (m, _, n, k, g, _) in enumerate(runs)])
     gemm_ops = np.array([2.0 * m * n * k for (m, _, n, k, g, _) in runs])
     table = []
@@ -344,7 +365,7 @@ def main():
     else:
         achieved = float(gemm_ops.mean()) / avg_dur / 1e12
         peak, unit, bound = INT8_PEAK_TOPS, "TFLOP/s", "mfma"
-    traffic = load_traffic(args.workload)
+    traffic = None if (args.w4a16 or args.static_scale is not None) else load_traffic(args.workload)
     value_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     value_tops = step_ops / (ms_per_step * 1e-3) / 1e12
     if hbm_bound:
@@ -363,7 +384,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "f16" if args.w4a16 else "int8",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -371,7 +392,8 @@ def main():
             "step": "every run: w4a8_linear fused (one launch) where it applies, "
                     "else w4a8_quant_act + w4a8_gemm",
             "fused_runs": int(sum(fused)),
-            "activation_scale": ("static per-tensor %g" % args.static_scale
+            "activation_scale": ("fp16 activations (W4A16 comparison)" if args.w4a16 else
+                                 "static per-tensor %g" % args.static_scale
                                  if args.static_scale is not None else "per-token dynamic"),
             "weight_rotation_copies": ncopies,
             "launch": "host-enqueued behind a GPU spin, events around every GEMM",

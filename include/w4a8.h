@@ -206,6 +206,23 @@ w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
                         int32_t* acc_dev, int ldacc, void* workspace_dev,
                         size_t workspace_bytes, const w4a8_gemm_opts* opts, void* stream);
 
+/* ----------------------------------------------------- W4A16 comparison
+ * The weight-only baseline the pages measure W4A8 against, on the same blob:
+ * fp16 activations times the fp16 weights W16^[n,k] = fp16(s1[n] * W8^[n,k])
+ * (one rounding), summed in fp32 on the fp16 MFMA:
+ *   Y[m,n] = fp16(sum_k A[m,k] * W16^[n,k])
+ * There is no activation quantization and no s_a.
+ *   a_dev   m x k fp16, row stride lda elements (lda >= k, lda % 8 == 0,
+ *           16-byte aligned); y_dev m x n fp16, row stride ldy >= n.
+ *   opts    NULL, or variant 0/1 with n_tiles / k_split as for the skinny
+ *           W4A8 kernel.
+ * Small M only (M <= 64, the weight-streaming regime).  Results are within
+ * the fp32 summation bound of the exact sum, not bit-exact across choices.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (shape, or m > 64), DEVICE. */
+w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
+                       const void* blob_dev, int n, int g, uint16_t* y_dev, int ldy,
+                       const w4a8_gemm_opts* opts, void* stream);
+
 /* Kernel launches w4a8_linear makes for these arguments: 1 (fused), 2
  * (quantizer + GEMM) or 3 (quantizer + GEMM split over K + reduction); 0 if
  * the call would be rejected.  Host only, no HIP call. */

@@ -305,3 +305,24 @@ def test_linear_launch_plan():
     assert L.w4a8_linear_launches(8, 4096, 4096, 128, ctypes.byref(opts)) == 1
     assert L.w4a8_linear_launches(9, 4096, 4096, 128, ctypes.byref(opts)) == 0
     assert L.w4a8_linear_launches(1, 4008, 4096, 128, None) == 0      # n % 16
+
+
+def test_w4a16_validates_before_any_hip_call():
+    L = w4.lib
+    fake = ctypes.c_void_p(4096)
+    # (a, lda, m, k, blob, n, g, y, ldy, opts, stream)
+    assert L.w4a16_gemm(fake, 512, 4, 512, fake, 250, 128, fake, 256, None, None) == 2   # n % 16
+    assert L.w4a16_gemm(fake, 512, 65, 512, fake, 256, 128, fake, 256, None, None) == 2  # m > 64
+    assert L.w4a16_gemm(fake, 516, 4, 512, fake, 256, 128, fake, 256, None, None) == 1   # lda % 8
+    assert L.w4a16_gemm(fake, 500, 4, 512, fake, 256, 128, fake, 256, None, None) == 1   # lda < k
+    assert L.w4a16_gemm(None, 512, 4, 512, fake, 256, 128, fake, 256, None, None) == 1
+    assert L.w4a16_gemm(ctypes.c_void_p(4104), 512, 4, 512, fake, 256, 128, fake, 256, None,
+                        None) == 1                                                    # misaligned
+    opts = w4.GemmOpts(2)
+    assert L.w4a16_gemm(fake, 512, 4, 512, fake, 256, 128, fake, 256, ctypes.byref(opts),
+                        None) == 1                                                    # no tiled
+    opts = w4.GemmOpts(1, 9)
+    assert L.w4a16_gemm(fake, 512, 4, 512, fake, 256, 128, fake, 256, ctypes.byref(opts),
+                        None) == 1                                                    # > 8 waves
+    assert L.w4a16_gemm(None, 512, 0, 512, None, 256, 128, None, 256, None, None) == 0
+

@@ -77,6 +77,7 @@ def _load():
         "w4a8_gemm": (I, [P, I, P, I, P, I, I, I, P, I, P, I, P, Z, P, P]),
         "w4a8_linear": (I, [P, I, I, I, P, I, I, P, I, P, I, P, P, I, P, Z, P, P]),
         "w4a8_linear_launches": (I, [I, I, I, I, P]),
+        "w4a16_gemm": (I, [P, I, I, I, P, I, I, P, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -256,3 +257,21 @@ def linear(a, blob_dev, n: int, k: int, g: int, y=None, a8=None, s_a=None, acc=N
                          ctypes.byref(opts) if opts is not None else None, _stream_ptr(stream))
     _check(st, "w4a8_linear")
     return (y, a8, s_a, acc) if acc is not None else (y, a8, s_a)
+
+
+def w4a16(a, blob_dev, n: int, k: int, g: int, y=None, variant: int = 0, k_split: int = 0,
+          n_tiles: int = 0, stream=None):
+    """W4A16 comparison GEMM on the same blob: fp16 A times fp16-decoded weights."""
+    torch = _torch()
+    assert a.dtype == torch.float16 and a.is_cuda and a.dim() == 2 and a.stride(1) == 1
+    m = a.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=a.device)
+    opts = None
+    if variant or k_split or n_tiles:
+        opts = GemmOpts(variant, k_split, n_tiles)
+    _check(lib.w4a16_gemm(a.data_ptr(), a.stride(0), m, k, blob_dev.data_ptr(), n, g,
+                          y.data_ptr(), y.stride(0),
+                          ctypes.byref(opts) if opts is not None else None, _stream_ptr(stream)),
+           "w4a16_gemm")
+    return y

@@ -45,7 +45,7 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    for src in ("skinny.hip", "tiled.hip", "quant_act.hip"):
+    for src in ("skinny.hip", "tiled.hip", "quant_act.hip", "w4a16.hip"):
         obj = os.path.join(BUILD, src + ".o")
         _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)

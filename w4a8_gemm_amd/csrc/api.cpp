@@ -327,6 +327,45 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
                    workspace_dev, workspace_bytes, opts, stream);
 }
 
+extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
+                                  const void* blob_dev, int n, int g, uint16_t* y_dev, int ldy,
+                                  const w4a8_gemm_opts* opts, void* stream) {
+  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
+  if (m == 0) return W4A8_OK;
+  if (!a_dev || !blob_dev || !y_dev) return W4A8_ERR_INVALID_ARGUMENT;
+  if (lda < k || lda % 8 || ldy < n) return W4A8_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
+  if (opts && (opts->variant > 1 || opts->variant < 0)) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m > 64) return W4A8_ERR_UNSUPPORTED;
+  // one row tile per workgroup (more row tiles go to grid.y): fp16 operands
+  // take twice the registers of int8 ones, and a deeper row tile would spill
+  SkinnyConfig c = choose_skinny(std::min(m, 16), n, k);
+  c.mr = 1;
+  if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
+  if (opts && opts->k_split > 0) {
+    c.kw = opts->k_split;
+    c.kbw = blocks_per_wave(k / kKBlock, c.kw);
+  }
+  const int gpb = groups_per_block(k, g);
+  if (!skinny_config_supported(c, k, gpb)) return W4A8_ERR_INVALID_ARGUMENT;
+  Sections sec = sections(n, k, g);
+  const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
+  Gemm16Params p{};
+  p.a = a_dev;
+  p.lda = lda;
+  p.m = m;
+  p.q = base + sec.q_off;
+  p.meta = base + sec.meta_off;
+  p.s1 = reinterpret_cast<const uint16_t*>(base + sec.s1_off);
+  p.n = n;
+  p.k = k;
+  p.meta_row_bytes = sec.meta_row_bytes;
+  p.y = y_dev;
+  p.ldy = ldy;
+  return device_status(launch_w4a16_skinny(p, gpb, c, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_opts* opts) {
   if (m <= 0 || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
   const int variant = opts ? opts->variant : 0;

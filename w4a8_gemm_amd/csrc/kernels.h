@@ -29,6 +29,21 @@ struct GemmParams {
 
 constexpr int kMaxSlices = 16;   // workgroups splitting K of one tile
 
+// W4A16 comparison GEMM on the same blob: fp16 activations, fp16 output.
+struct Gemm16Params {
+  const uint16_t* a;     // m x k fp16, row stride lda elements
+  int lda;
+  int m;
+  const uint8_t* q;
+  const uint8_t* meta;
+  const uint16_t* s1;
+  int n, k;
+  int meta_row_bytes;
+  uint16_t* y;
+  int ldy;
+  int kb_per_wave;
+};
+
 // Groups per 128-k block: 1, 2 or 4 for g = 128, 64, 32; 0 in per-channel mode.
 inline int groups_per_block(int k, int g) {
   if (g == 0 || g == k) return 0;
@@ -64,6 +79,9 @@ hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
                              hipStream_t stream);
 hipError_t launch_split_reduce(const GemmParams& p, int slices, hipStream_t stream);
 bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb);
+
+hipError_t launch_w4a16_skinny(const Gemm16Params& p, int gpb, const SkinnyConfig& c,
+                               hipStream_t stream);
 
 // Fused quantization + skinny GEMM: M <= kFusedMaxRows, one row tile, each
 // wave's K range at most 16 blocks, LDS within kFusedMaxLds.  The automatic
