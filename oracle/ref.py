@@ -150,13 +150,49 @@ def per_channel(w: np.ndarray):
             np.ones((n, 1), dtype=np.uint8))
 
 
+# ---------------------------------------------------------------- O1'' codebook
+NF_CODE = 1   # the "group size" value that selects the codebook mode
+
+
+def nf_codebook() -> np.ndarray:
+    """The 16 int8 levels of the non-uniform (NormalFloat-style) 4-bit code,
+    FLUTE page, section 方法详解 (LUT-quantized weights, NormalFloat).  The
+    page prints no levels; reading: the standard-normal quantiles at the 16
+    probabilities (i + 1/2) / 16, scaled so the largest is 119 (the level-1
+    int8 range) and rounded half-to-even to integers."""
+    from scipy.stats import norm
+    z = norm.ppf((np.arange(16) + 0.5) / 16.0)
+    return np.rint(119.0 * z / z[-1]).astype(np.int32)
+
+
+def nf_nearest(w8: np.ndarray, lut: np.ndarray) -> np.ndarray:
+    """Index of the codebook level nearest to each int8 value; ties go to the
+    lower index."""
+    d = np.abs(np.asarray(w8, np.int64)[..., None] - lut.astype(np.int64))
+    return np.argmin(d, axis=-1).astype(np.uint8)    # argmin keeps the first minimum
+
+
+def quantize_weights_nf(w: np.ndarray):
+    """O1'' codebook mode, per output row: the level-1 int8 quantization O1
+    (s1 = fp16(absmax / 119)), then each int8 value replaced by the nearest
+    level of nf_codebook(); the decoded weight is LUT[q]."""
+    w = np.ascontiguousarray(w, dtype=F32)
+    s1, w8 = level1_rows(w)
+    lut = nf_codebook()
+    return {"q": nf_nearest(w8, lut), "s1": s1, "lut": lut, "g_eff": NF_CODE}
+
+
 # ---------------------------------------------------------------- O1 + O2
 def quantize_weights(w: np.ndarray, g: int):
-    """Progressive quantization of W (N x K fp32); g = 0 or g = K is per-channel.
+    """Progressive quantization of W (N x K fp32); g = 0 or g = K is per-channel,
+    g = NF_CODE the codebook mode.
 
     Returns a dict with q uint8[N,K], z uint8[N,G], s2 uint8[N,G],
-    s1 float16[N] and g_eff (the group length used by decode).
+    s1 float16[N] and g_eff (the group length used by decode); the codebook
+    mode returns q, s1 and the lut instead of z and s2.
     """
+    if g == NF_CODE:
+        return quantize_weights_nf(w)
     w = np.ascontiguousarray(w, dtype=F32)
     n, k = w.shape
     if g == 0 or g == k:
@@ -170,6 +206,8 @@ def quantize_weights(w: np.ndarray, g: int):
 
 
 def decoded_weights(qw: dict) -> np.ndarray:
+    if "lut" in qw:
+        return qw["lut"][qw["q"].astype(np.int64)].astype(np.int32)
     return decode(qw["q"], qw["z"], qw["s2"], qw["g_eff"])
 
 

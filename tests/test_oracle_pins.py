@@ -613,3 +613,96 @@ def test_w4a16_pins_catch_mutants():
             acc = (acc + (a[:, kk:kk + 1].astype(np.float16) * w16[:, kk][None, :]).astype(np.float16))
         return acc, w16, sa
     assert w4a16_brute_check(y_fp16_accumulate) > 0
+
+
+# ------------------------------------------------------------ O1'' codebook mode
+def _inv_normal_cdf(p: float) -> float:
+    """Standard-normal quantile by bisection on math.erf (independent of scipy)."""
+    import math
+    lo, hi = -10.0, 10.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if 0.5 * (1.0 + math.erf(mid / math.sqrt(2.0))) < p:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def test_nf_codebook_from_its_definition():
+    lut = ref.nf_codebook()
+    z = [_inv_normal_cdf((i + 0.5) / 16) for i in range(16)]
+    want = [int(round(119.0 * v / z[-1])) for v in z]      # no exact .5 ties occur
+    assert lut.tolist() == want
+    assert (np.diff(lut) > 0).all() and (lut == -lut[::-1]).all() and lut[-1] == 119
+
+
+def nf_nearest_check(fn):
+    """Exhaustive over every level-1 value: the chosen level is a nearest one,
+    and the lowest index among equally near ones.  Returns violations."""
+    lut = [int(v) for v in ref.nf_codebook()]
+    w8 = np.arange(-119, 120)
+    q = fn(w8, np.array(lut))
+    bad = 0
+    for v, j in zip(w8.tolist(), q.tolist()):
+        dist = [abs(level - v) for level in lut]
+        best = min(dist)
+        if dist[j] != best or j != dist.index(best):
+            bad += 1
+    return bad
+
+
+def test_nf_nearest_exhaustive():
+    assert nf_nearest_check(ref.nf_nearest) == 0
+
+
+def nf_golden_check(fn):
+    bad = []
+    lut = ref.nf_codebook()
+    with open(os.path.join(GOLDEN, "nf_cases.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            w8, idx, dec = (int(x) for x in line.split("|"))
+            j = int(fn(np.array([w8]), lut)[0])
+            if j != idx or int(lut[j]) != dec:
+                bad.append(line.strip())
+    return bad
+
+
+def test_nf_golden():
+    assert nf_golden_check(ref.nf_nearest) == []
+
+
+def test_nf_whole_rows():
+    """Codebook mode on rows: decoded weights are codebook levels, s1 is the
+    level-1 scale, and the GEMM of the decoded weights matches brute force."""
+    w = synth.weights(16, 256, seed=77, dist="student_t4")
+    qw = ref.quantize_weights(w, ref.NF_CODE)
+    s1, w8 = ref.level1_rows(np.asarray(w, np.float32))
+    assert np.array_equal(qw["s1"].view(np.uint16), s1.view(np.uint16))
+    dec = ref.decoded_weights(qw)
+    assert set(np.unique(dec).tolist()) <= set(ref.nf_codebook().tolist())
+    assert (np.abs(dec - w8) <= 17).all()        # half the widest level gap (119 - 84 = 35)
+    a8 = np.random.default_rng(3).integers(-127, 128, (3, 256))
+    acc = ref.gemm_acc(a8, dec)
+    brute = np.array([[sum(int(a8[m, kk]) * int(dec[n, kk]) for kk in range(256))
+                       for n in range(16)] for m in range(3)])
+    assert np.array_equal(acc, brute)
+
+
+def test_nf_pins_catch_mutants():
+    def ties_up(w8, lut):
+        d = np.abs(np.asarray(w8, np.int64)[..., None] - lut.astype(np.int64))
+        return (15 - np.argmin(d[..., ::-1], axis=-1)).astype(np.uint8)
+
+    def truncate_toward_zero(w8, lut):
+        w8 = np.asarray(w8, np.int64)
+        out = np.zeros(w8.shape, np.uint8)
+        for i, v in enumerate(w8.ravel()):
+            cands = [j for j in range(16) if abs(int(lut[j])) <= abs(v) and np.sign(lut[j]) == np.sign(v)]
+            out.ravel()[i] = cands[-1] if v > 0 and cands else (cands[0] if cands else 7)
+        return out
+
+    for mutant in (ties_up, truncate_toward_zero):
+        assert nf_nearest_check(mutant) > 0 or nf_golden_check(mutant), mutant.__name__
