@@ -35,15 +35,24 @@ CSRC = os.path.join(ROOT, "w4a8_gemm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
+CODEBOOK_NF = 1   # g value of the non-uniform codebook mode (no meta)
+
+
+def meta_bytes(n, k, g):
+    if g == CODEBOOK_NF:
+        return 0.0
+    return 0.5 * n if g in (0, k) else 1.5 * n * k / g
+
+
 def algo_bytes(m, n, k, g):
     """Bytes the method must move: codes, group meta, s1, A8, s_a, Y."""
-    meta = 0.5 * n if g in (0, k) else 1.5 * n * k / g
+    meta = meta_bytes(n, k, g)
     return n * k / 2 + meta + 2 * n + m * k + 2 * m + 2 * m * n
 
 
 def w4a16_bytes(m, n, k, g):
     """The W4A16 comparison GEMM: the same weight bytes, fp16 A in, fp16 Y out."""
-    meta = 0.5 * n if g in (0, k) else 1.5 * n * k / g
+    meta = meta_bytes(n, k, g)
     return n * k / 2 + meta + 2 * n + 2 * m * k + 2 * m * n
 
 
@@ -176,6 +185,9 @@ def main():
     ap.add_argument("--w4a16", action="store_true",
                     help="time the W4A16 comparison GEMM (same packed weights, fp16 "
                          "activations) in place of the W4A8 layer; M <= 64 workloads")
+    ap.add_argument("--codebook", action="store_true",
+                    help="pack every layer in the non-uniform codebook mode (register "
+                         "table decode) instead of the workload's group size")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
@@ -198,6 +210,8 @@ def main():
     wl_names = list(synth.workloads().keys())
     items = synth.workloads()[args.workload]
     cfg_idx = wl_names.index(args.workload)
+    if args.codebook:
+        items = [(c, m, layer, n, k, CODEBOOK_NF, dist) for (c, m, layer, n, k, g, dist) in items]
 
     # weights: one per (layer, g); seeds as the parity tests use them
     layer_keys = []
@@ -365,7 +379,8 @@ def main():
     else:
         achieved = float(gemm_ops.mean()) / avg_dur / 1e12
         peak, unit, bound = INT8_PEAK_TOPS, "TFLOP/s", "mfma"
-    traffic = None if (args.w4a16 or args.static_scale is not None) else load_traffic(args.workload)
+    traffic = (None if (args.w4a16 or args.codebook or args.static_scale is not None)
+               else load_traffic(args.workload))
     value_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     value_tops = step_ops / (ms_per_step * 1e-3) / 1e12
     if hbm_bound:
@@ -392,6 +407,7 @@ def main():
             "step": "every run: w4a8_linear fused (one launch) where it applies, "
                     "else w4a8_quant_act + w4a8_gemm",
             "fused_runs": int(sum(fused)),
+            "weights": "codebook (NormalFloat-style levels)" if args.codebook else "uniform groups",
             "activation_scale": ("fp16 activations (W4A16 comparison)" if args.w4a16 else
                                  "static per-tensor %g" % args.static_scale
                                  if args.static_scale is not None else "per-token dynamic"),

@@ -59,9 +59,19 @@ typedef enum {
 /* Group-size value that selects per-channel mode (one scale and zero per row). */
 #define W4A8_GROUP_PER_CHANNEL 0
 
+/* Group-size value that selects the non-uniform codebook mode (the
+ * LUT-quantized, NormalFloat-style weights of the FLUTE page): per row the
+ * level-1 int8 quantization (fp16 s1), then each int8 value replaced by the
+ * code of the nearest of 16 fixed int8 levels (ties to the lower code):
+ *   -119 -84 -65 -50 -37 -26 -15 -5 5 15 26 37 50 65 84 119
+ * (standard-normal quantiles at (i + 1/2)/16 scaled to 119).  W8^ = level[q];
+ * the decode is a register table lookup.  No groups, no meta section. */
+#define W4A8_CODEBOOK_NF 1
+
 /* Shape limits.  K must be a multiple of W4A8_K_QUANTUM, N of W4A8_N_QUANTUM;
  * K <= W4A8_K_MAX keeps every int32 accumulator exact (127*128*K < 2^31).
- * g must be 32, 64 or 128 (and divide K), or W4A8_GROUP_PER_CHANNEL (or K). */
+ * g must be 32, 64 or 128 (and divide K), W4A8_GROUP_PER_CHANNEL (or K), or
+ * W4A8_CODEBOOK_NF. */
 #define W4A8_K_QUANTUM 128
 #define W4A8_N_QUANTUM 16
 #define W4A8_K_MAX 131072
@@ -84,6 +94,7 @@ const char* w4a8_last_device_error(void);
  *   meta  N*G4 bytes, G4 = (groups per row) rounded up to a multiple of 4:
  *         row n holds one byte per group (low nibble z, high nibble s2 - 1)
  *         at n*G4 + group; padding bytes are 0.  Per-channel mode: 1 group.
+ *         Codebook mode: empty (the header holds the 16 levels at byte 56).
  *   s1    N fp16 row scales.
  * The blob is position independent: copy it verbatim to device memory and
  * pass that copy to w4a8_gemm.  Device code never reads the header.       */
@@ -104,8 +115,9 @@ w4a8_status w4a8_blob_info(const void* blob, size_t blob_bytes,
                            int* n, int* k, int* g);
 
 /* Decode a host blob back to logical arrays (for checking): q[n*k] codes,
- * z[n*G] and s2[n*G] per group (G = k/g, or 1 per channel), s1[n] fp16 bits.
- * Any output pointer may be NULL to skip it.  Errors: INVALID_ARGUMENT, LAYOUT. */
+ * z[n*G] and s2[n*G] per group (G = k/g, or 1 per channel, or 0 in codebook
+ * mode: nothing written), s1[n] fp16 bits.  Any output pointer may be NULL
+ * to skip it.  Errors: INVALID_ARGUMENT, LAYOUT. */
 w4a8_status w4a8_unpack(const void* blob, size_t blob_bytes,
                         uint8_t* q, uint8_t* z, uint8_t* s2, uint16_t* s1);
 

@@ -65,6 +65,23 @@ def test_pack_matches_oracle(dist, g):
     _compare_with_oracle(w, g)
 
 
+@pytest.mark.parametrize("dist", ["normal", "student_t4"])
+def test_pack_codebook_matches_oracle(dist):
+    """Codebook mode: codes, s1 and the level table in the header equal the
+    oracle's (its levels derived from the normal quantiles)."""
+    w = synth.weights(128, 1024, seed=90, dist=dist)
+    blob = w4.pack(w, w4.CODEBOOK_NF)
+    got = w4.unpack(blob)
+    want = ref.quantize_weights(w, ref.NF_CODE)
+    assert got["g"] == w4.CODEBOOK_NF and got["z"].shape == (128, 0)
+    assert np.array_equal(got["q"], want["q"])
+    assert np.array_equal(got["s1"].view(np.uint16), want["s1"].view(np.uint16))
+    assert np.array_equal(got["levels"], want["lut"])
+    assert w4.packed_size(128, 1024, w4.CODEBOOK_NF) == 256 + 128 * 1024 // 2 + 256
+    # the independent layout reader sees the same codes
+    assert np.array_equal(_decode_layout(blob)[0], want["q"])
+
+
 def test_pack_matches_oracle_special_rows():
     w = synth.weights(64, 512, seed=77)
     w[0] = 0.0                                  # zero row
@@ -83,7 +100,7 @@ def test_pack_matches_oracle_special_rows():
 def _decode_layout(blob):
     """Independent reader of the documented layout v1 (test-side)."""
     n, k, g = w4.blob_info(blob)
-    groups = 1 if g == 0 else k // g
+    groups = 1 if g == 0 else (0 if g == w4.CODEBOOK_NF else k // g)
     qsec = blob[256:256 + n * k // 2]
     kb = k // 128
     # reshape to [tile][kblock][lane][16 bytes]

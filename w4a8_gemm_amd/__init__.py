@@ -107,6 +107,10 @@ def status_string(status: int) -> str:
 
 
 # ------------------------------------------------------------------ host side
+GROUP_PER_CHANNEL = 0
+CODEBOOK_NF = 1      # g value of the non-uniform codebook mode
+
+
 def packed_size(n: int, k: int, g: int) -> int:
     return int(lib.w4a8_packed_size(n, k, g))
 
@@ -134,14 +138,17 @@ def blob_info(blob: np.ndarray) -> tuple[int, int, int]:
 def unpack(blob: np.ndarray) -> dict:
     """Logical arrays of a host blob: q [N,K], z/s2 [N,G], s1 [N] (float16)."""
     n, k, g = blob_info(blob)
-    groups = 1 if g == 0 else k // g
+    groups = 1 if g == 0 else (0 if g == CODEBOOK_NF else k // g)
     q = np.empty((n, k), dtype=np.uint8)
     z = np.empty((n, groups), dtype=np.uint8)
     s2 = np.empty((n, groups), dtype=np.uint8)
     s1 = np.empty(n, dtype=np.uint16)
     _check(lib.w4a8_unpack(blob.ctypes.data, blob.nbytes, q.ctypes.data, z.ctypes.data,
                            s2.ctypes.data, s1.ctypes.data), "w4a8_unpack")
-    return {"q": q, "z": z, "s2": s2, "s1": s1.view(np.float16), "n": n, "k": k, "g": g}
+    out = {"q": q, "z": z, "s2": s2, "s1": s1.view(np.float16), "n": n, "k": k, "g": g}
+    if g == CODEBOOK_NF:
+        out["levels"] = blob[56:72].view(np.int8).astype(np.int32)
+    return out
 
 
 # ------------------------------------------------------------------ device side

@@ -26,7 +26,7 @@ w4a8_status device_status(hipError_t e) {
 
 bool gemm_shape_supported(int n, int k, int g) {
   if (n % kColTile || k % kKBlock || k > W4A8_K_MAX) return false;
-  if (g == W4A8_GROUP_PER_CHANNEL || g == k) return true;
+  if (g == W4A8_GROUP_PER_CHANNEL || g == k || g == W4A8_CODEBOOK_NF) return true;
   return (g == 32 || g == 64 || g == 128) && k % g == 0;
 }
 
@@ -294,7 +294,7 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const SkinnyConfig fc = fused_plan(m, n, k, opts);
-  const bool fused_ok = fused_config_supported(fc, m, k);
+  const bool fused_ok = g != W4A8_CODEBOOK_NF && fused_config_supported(fc, m, k);
   if (variant == 3 && !fused_ok) return W4A8_ERR_UNSUPPORTED;
   if (variant == 3 || (variant == 0 && fused_ok && m <= kFusedAutoRows)) {
     Sections sec = sections(n, k, g);
@@ -337,7 +337,7 @@ extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
   if (lda < k || lda % 8 || ldy < n) return W4A8_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
   if (opts && (opts->variant > 1 || opts->variant < 0)) return W4A8_ERR_INVALID_ARGUMENT;
-  if (m > 64) return W4A8_ERR_UNSUPPORTED;
+  if (m > 64 || g == W4A8_CODEBOOK_NF) return W4A8_ERR_UNSUPPORTED;
   // one row tile per workgroup (more row tiles go to grid.y): fp16 operands
   // take twice the registers of int8 ones, and a deeper row tile would spill
   SkinnyConfig c = choose_skinny(std::min(m, 16), n, k);
@@ -370,7 +370,8 @@ extern "C" int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_
   if (m <= 0 || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
   const int variant = opts ? opts->variant : 0;
   if (variant < 0 || variant > 3) return 0;
-  const bool fused_ok = fused_config_supported(fused_plan(m, n, k, opts), m, k);
+  const bool fused_ok =
+      g != W4A8_CODEBOOK_NF && fused_config_supported(fused_plan(m, n, k, opts), m, k);
   if (variant == 3) return fused_ok ? 1 : 0;
   if (variant == 0 && fused_ok && m <= kFusedAutoRows) return 1;
   return plan_gemm(m, n, k, opts).slices > 1 ? 3 : 2;

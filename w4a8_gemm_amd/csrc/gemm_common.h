@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "codebook.h"
 #include "kernels.h"
 #include "quant_common.h"
 
@@ -109,6 +110,28 @@ __device__ __forceinline__ void store_frag(const GemmParams& p, int row0, int co
       if (p.acc) p.acc[size_t(row) * p.ldacc + col] = v[r];
     }
   }
+}
+
+// Codebook mode: four codes (one per byte, low 4 bits selected by `sel`,
+// bit 3 by `pick`) to their int8 levels with three byte permutes: the low
+// and high halves of the 16-entry table each give a candidate byte, and the
+// code's bit 3 chooses between them.
+//   sel  = code & 7 in every byte
+//   pick = byte index i, plus 4 where the code's bit 3 is set
+__device__ __forceinline__ uint32_t lut4(uint32_t sel, uint32_t pick) {
+  const uint32_t lo = __builtin_amdgcn_perm(nf_dword(1), nf_dword(0), sel);   // levels 0..7
+  const uint32_t hi = __builtin_amdgcn_perm(nf_dword(3), nf_dword(2), sel);   // levels 8..15
+  return __builtin_amdgcn_perm(hi, lo, pick);
+}
+
+// Two packed words (16 codes) -> one B operand, codebook mode.
+__device__ __forceinline__ v4i decode16_lut(uint32_t w0, uint32_t w1) {
+  v4i b;
+  b[0] = int(lut4(w0 & 0x07070707u, ((w0 >> 1) & 0x04040404u) | 0x03020100u));
+  b[1] = int(lut4((w0 >> 4) & 0x07070707u, ((w0 >> 5) & 0x04040404u) | 0x03020100u));
+  b[2] = int(lut4(w1 & 0x07070707u, ((w1 >> 1) & 0x04040404u) | 0x03020100u));
+  b[3] = int(lut4((w1 >> 4) & 0x07070707u, ((w1 >> 5) & 0x04040404u) | 0x03020100u));
+  return b;
 }
 
 // Meta byte of group `grp` for a lane whose row pointer is mrow.

@@ -44,8 +44,10 @@ struct Gemm16Params {
   int kb_per_wave;
 };
 
-// Groups per 128-k block: 1, 2 or 4 for g = 128, 64, 32; 0 in per-channel mode.
+// Groups per 128-k block: 1, 2 or 4 for g = 128, 64, 32; 0 in per-channel
+// mode; -1 in the codebook mode (g == 1: no groups, no meta).
 inline int groups_per_block(int k, int g) {
+  if (g == 1) return -1;
   if (g == 0 || g == k) return 0;
   return 128 / g;
 }

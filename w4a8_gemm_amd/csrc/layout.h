@@ -11,6 +11,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "codebook.h"
+
 namespace w4a8 {
 
 constexpr int kKBlock = 128;     // k covered by one 16-byte lane chunk (2 MFMA k-steps)
@@ -33,11 +35,18 @@ struct Sections {
   int meta_row_bytes; // groups per row rounded up to a multiple of 4
 };
 
+// In the codebook mode (g == kCodebookG) there are no groups and no meta
+// section: a code decodes through the fixed level table alone.
 inline Sections sections(int n, int k, int g) {
   Sections s;
-  int ge = effective_group(k, g);
-  s.groups = k / ge;
-  s.meta_row_bytes = (s.groups + 3) & ~3;
+  if (g == kCodebookG) {
+    s.groups = 0;
+    s.meta_row_bytes = 0;
+  } else {
+    int ge = effective_group(k, g);
+    s.groups = k / ge;
+    s.meta_row_bytes = (s.groups + 3) & ~3;
+  }
   s.q_off = kHeaderBytes;
   s.q_bytes = size_t(n) * size_t(k) / 2;
   s.meta_off = s.q_off + align256(s.q_bytes);

@@ -82,13 +82,27 @@ int div_rne(int a, int b) {
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Quantize one row into logical codes q[k], and per-group z / s2.
-w4a8_status quantize_row(const float* w, int k, int ge, uint8_t* q, uint8_t* z, uint8_t* s2,
-                         uint16_t* s1_bits, std::vector<int>& w8) {
+// Nearest codebook level to an int8 value, ties to the lower code.
+uint8_t nearest_level(int v) {
+  int best = 0, dist = 1 << 30;
+  for (int j = 0; j < 16; ++j) {
+    const int d = std::abs(int(kNfLevels[j]) - v);
+    if (d < dist) {
+      dist = d;
+      best = j;
+    }
+  }
+  return uint8_t(best);
+}
+
+// Quantize one row into logical codes q[k], and per-group z / s2 (codebook
+// mode: level-1 int8, then the nearest level's code; no z / s2).
+w4a8_status quantize_row(const float* w, int k, int ge, bool codebook, uint8_t* q, uint8_t* z,
+                         uint8_t* s2, uint16_t* s1_bits, std::vector<int>& w8) {
   for (int i = 0; i < k; ++i)
     if (!std::isfinite(w[i])) return W4A8_ERR_NONFINITE;
 
-  if (ge == k) {  // per-channel: one uint4 step (fp16) and zero per row
+  if (ge == k && !codebook) {  // per-channel: one uint4 step (fp16) and zero per row
     float lo = 0.0f, hi = 0.0f;
     for (int i = 0; i < k; ++i) {
       lo = std::min(lo, w[i]);
@@ -125,6 +139,10 @@ w4a8_status quantize_row(const float* w, int k, int ge, uint8_t* q, uint8_t* z, 
     float r = 1.0f / sf;
     for (int i = 0; i < k; ++i) w8[i] = clampi(int(std::nearbyint(w[i] * r)), -119, 119);
   }
+  if (codebook) {
+    for (int i = 0; i < k; ++i) q[i] = nearest_level(w8[i]);
+    return W4A8_OK;
+  }
   // level 2: uint4 per group with integer step and zero
   for (int g0 = 0, gi = 0; g0 < k; g0 += ge, ++gi) {
     int lo = 0, hi = 0;
@@ -144,7 +162,7 @@ w4a8_status quantize_row(const float* w, int k, int ge, uint8_t* q, uint8_t* z, 
 bool shape_ok(int n, int k, int g) {
   if (n <= 0 || k <= 0) return false;
   if (n % kColTile || k % kKBlock || k > W4A8_K_MAX) return false;
-  if (g == 0 || g == k) return true;
+  if (g == 0 || g == k || g == kCodebookG) return true;
   if (g != 32 && g != 64 && g != 128) return false;
   return k % g == 0;
 }
@@ -152,8 +170,9 @@ bool shape_ok(int n, int k, int g) {
 struct Header {
   char magic[8];
   uint32_t version;
-  int32_t n, k, g;  // g == 0: per-channel
+  int32_t n, k, g;  // g == 0: per-channel; g == kCodebookG: codebook mode
   uint64_t q_off, meta_off, s1_off, total;
+  int8_t levels[16];  // codebook mode: the level of each code (else zero)
 };
 
 }  // namespace
@@ -169,8 +188,9 @@ extern "C" w4a8_status w4a8_pack(const float* w, int n, int k, int ldw, int g, v
   if (!shape_ok(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   Sections sec = sections(n, k, g);
   if (blob_bytes < sec.total) return W4A8_ERR_BUFFER_TOO_SMALL;
-  const int ge = effective_group(k, g);
-  const int groups = sec.groups;
+  const bool codebook = g == kCodebookG;
+  const int ge = codebook ? k : effective_group(k, g);
+  const int groups = std::max(1, sec.groups);
   const int kblocks = k / kKBlock;
 
   uint8_t* base = static_cast<uint8_t*>(blob);
@@ -195,15 +215,15 @@ extern "C" w4a8_status w4a8_pack(const float* w, int n, int k, int ldw, int g, v
       for (int r = 0; r < kColTile; ++r) {
         int row = t * kColTile + r;
         uint16_t s1b = 0;
-        w4a8_status st = quantize_row(w + size_t(row) * size_t(ldw), k, ge, q.data(), z.data(),
-                                      s2.data(), &s1b, w8);
+        w4a8_status st = quantize_row(w + size_t(row) * size_t(ldw), k, ge, codebook, q.data(),
+                                      z.data(), s2.data(), &s1b, w8);
         if (st != W4A8_OK) {
           int expected = W4A8_OK;
           first_error.compare_exchange_strong(expected, int(st));
           return;
         }
         s1sec[row] = s1b;
-        for (int gi = 0; gi < groups; ++gi)
+        for (int gi = 0; gi < sec.groups; ++gi)
           msec[meta_position(row, gi, sec.meta_row_bytes)] = uint8_t((z[gi] & 15u) | ((s2[gi] - 1u) << 4));
         for (int kk = 0; kk < k; ++kk) {
           size_t byte;
@@ -229,11 +249,12 @@ extern "C" w4a8_status w4a8_pack(const float* w, int n, int k, int ldw, int g, v
   h.version = kLayoutVersion;
   h.n = n;
   h.k = k;
-  h.g = (ge == k) ? 0 : g;
+  h.g = codebook ? kCodebookG : ((ge == k) ? 0 : g);
   h.q_off = sec.q_off;
   h.meta_off = sec.meta_off;
   h.s1_off = sec.s1_off;
   h.total = sec.total;
+  if (codebook) std::memcpy(h.levels, kNfLevels, 16);
   std::memcpy(base, &h, sizeof(h));
   return W4A8_OK;
 }

@@ -31,7 +31,8 @@ using namespace dev;
 // memory stream.  Partial int32 tiles of the KW waves are summed exactly
 // through LDS (split-K inside the workgroup: no workspace, no atomics).
 //
-// GPB = groups per 128-k block (1, 2, 4 for g = 128, 64, 32; 0 per channel).
+// GPB = groups per 128-k block (1, 2, 4 for g = 128, 64, 32; 0 per channel;
+// -1 codebook mode: no meta, codes decode through the level table).
 // The meta dword loaded for block kb holds every group the block uses.
 template <int MR, int NC, int GPB, int D>
 __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
   // blocks).  Meta loads land in mdn (next group) and become md (current
   // group) once the current group has been decoded, because the slots of a
   // group that share a dword are decoded after slot 0 has been refilled.
-  constexpr int MSTEP = GPB == 0 ? D : 4 / GPB;   // slots per meta dword
+  constexpr int MSTEP = GPB <= 0 ? D : 4 / GPB;   // slots per meta dword
   u32x4 q[D][NC];
   uint32_t md[D][NC], mdn[D][NC];
   v4i a[D][MR][2];
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       q[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qptr[c] + size_t(kb) * 1024));
-    if (j % MSTEP == 0) {
+    if (GPB >= 0 && j % MSTEP == 0) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) mdn[j][c] = mrow[c][GPB == 0 ? 0 : (kb * GPB) >> 2];
     }
@@ -109,6 +110,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
     }
   };
   auto next_group_meta = [&]() {
+    if (GPB < 0) return;
 #pragma unroll
     for (int j = 0; j < D; j += MSTEP)
 #pragma unroll
@@ -130,10 +132,14 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
       v4i bf[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const GroupConst gc = group_const((ms[c] >> (8 * byte)) & 0xFFu);
         const uint32_t w0 = h ? qs[c].z : qs[c].x;
         const uint32_t w1 = h ? qs[c].w : qs[c].y;
-        bf[c] = decode16(w0, w1, gc);
+        if constexpr (GPB < 0) {
+          bf[c] = decode16_lut(w0, w1);
+        } else {
+          const GroupConst gc = group_const((ms[c] >> (8 * byte)) & 0xFFu);
+          bf[c] = decode16(w0, w1, gc);
+        }
       }
 #pragma unroll
       for (int i = 0; i < MR; ++i)
@@ -487,6 +493,7 @@ hipError_t launch_skinny(const GemmParams& p, const SkinnyConfig& c, hipStream_t
 template <int MR, int NC>
 hipError_t skinny_by_gpb(const GemmParams& p, int gpb, const SkinnyConfig& c, hipStream_t s) {
   switch (gpb) {
+    case -1: return launch_skinny<MR, NC, -1>(p, c, s);
     case 0: return launch_skinny<MR, NC, 0>(p, c, s);
     case 1: return launch_skinny<MR, NC, 1>(p, c, s);
     case 2: return launch_skinny<MR, NC, 2>(p, c, s);

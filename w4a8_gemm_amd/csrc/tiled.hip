@@ -112,7 +112,8 @@ __global__ __launch_bounds__(64 * kColGroups * RW * KG, 2 / (RW * KG)) void tile
   static_assert(STAGE == tiled_stage_bytes<MR, NC, RW, KG>(), "stage layout");
   constexpr int CPW = BM * 8 / (64 * KWAVES);    // activation chunks per lane
   constexpr int NCL = NC / RW;                   // column tiles whose codes this wave loads
-  constexpr int LOADS = CPW + 2 * NCL;           // vector-memory ops per lane per stage
+  // vector-memory ops per lane per stage (codebook mode, GPB < 0: no meta)
+  constexpr int LOADS = CPW + (GPB < 0 ? 1 : 2) * NCL;
   static_assert(CPW >= 1 && BM * 8 % (64 * KWAVES) == 0, "tile must split evenly over lanes");
   static_assert(NCL >= 1 && NC % RW == 0, "code loads split evenly over row groups");
   static_assert(S >= 2 && (S - 2) * LOADS < 64, "vmcnt range");
@@ -203,10 +204,12 @@ __global__ __launch_bounds__(64 * kColGroups * RW * KG, 2 / (RW * KG)) void tile
     for (int c = 0; c < NCL; ++c)
       buffer_to_lds16(q_rsrc, st + A_BYTES + (cg * NC + rg * NCL + c) * 1024, q_lane,
                       q_tile[c] + uint32_t(kb) * 1024u);
+    if (GPB >= 0) {
 #pragma unroll
-    for (int c = 0; c < NCL; ++c)
-      buffer_to_lds4(m_rsrc, st + A_BYTES + W_BYTES + (cg * NC + rg * NCL + c) * 256, m_lane,
-                     m_tile[c] + (GPB == 0 ? 0u : uint32_t((kb * GPB) >> 2) * 4u));
+      for (int c = 0; c < NCL; ++c)
+        buffer_to_lds4(m_rsrc, st + A_BYTES + W_BYTES + (cg * NC + rg * NCL + c) * 256, m_lane,
+                       m_tile[c] + (GPB == 0 ? 0u : uint32_t((kb * GPB) >> 2) * 4u));
+    }
   };
 
   auto compute = [&](int kb, const uint8_t* st) {
@@ -215,11 +218,11 @@ __global__ __launch_bounds__(64 * kColGroups * RW * KG, 2 / (RW * KG)) void tile
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       qv[c] = *reinterpret_cast<const u32x4*>(st + w_off + c * 1024);
-      mv[c] = *reinterpret_cast<const uint32_t*>(st + m_off + c * 256);
+      mv[c] = GPB >= 0 ? *reinterpret_cast<const uint32_t*>(st + m_off + c * 256) : 0u;
     }
     // g >= 128 or per channel: both halves of the block share one group
     GroupConst gblk[NC];
-    if (GPB <= 1) {
+    if (GPB >= 0 && GPB <= 1) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         gblk[c] = group_const((mv[c] >> (GPB == 1 ? 8 * (kb & 3) : 0)) & 0xFFu);
@@ -232,10 +235,15 @@ __global__ __launch_bounds__(64 * kColGroups * RW * KG, 2 / (RW * KG)) void tile
       v4i bf[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const GroupConst gc = GPB <= 1 ? gblk[c] : group_const((mv[c] >> (8 * byte)) & 0xFFu);
         const uint32_t w0 = h ? qv[c].z : qv[c].x;
         const uint32_t w1 = h ? qv[c].w : qv[c].y;
-        bf[c] = decode16(w0, w1, gc);
+        if constexpr (GPB < 0) {
+          bf[c] = decode16_lut(w0, w1);
+        } else {
+          const GroupConst gc =
+              GPB <= 1 ? gblk[c] : group_const((mv[c] >> (8 * byte)) & 0xFFu);
+          bf[c] = decode16(w0, w1, gc);
+        }
       }
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
@@ -363,6 +371,7 @@ hipError_t launch_tiled_t(const GemmParams& p, int slices, hipStream_t stream) {
 template <int MR, int NC, int RW, int KG, int S>
 hipError_t tiled_by_gpb(const GemmParams& p, int gpb, int sl, hipStream_t s) {
   switch (gpb) {
+    case -1: return launch_tiled_t<MR, NC, RW, KG, -1, S>(p, sl, s);
     case 0: return launch_tiled_t<MR, NC, RW, KG, 0, S>(p, sl, s);
     case 1: return launch_tiled_t<MR, NC, RW, KG, 1, S>(p, sl, s);
     case 2: return launch_tiled_t<MR, NC, RW, KG, 2, S>(p, sl, s);
