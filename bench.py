@@ -37,6 +37,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 CODEBOOK_NF = 1   # g value of the non-uniform codebook mode (no meta)
 
+# sources of the kernels each counter entry covers (small M: fused and
+# skinny; large M: tiled with its K-split reduction)
+SKINNY_SOURCES = ["fused.hip", "skinny.hip", "gemm_common.h", "quant_common.h", "codebook.h"]
+TILED_SOURCES = ["tiled.hip", "gemm_common.h", "quant_common.h", "codebook.h"]
+
 
 def meta_bytes(n, k, g):
     if g == CODEBOOK_NF:
@@ -178,7 +183,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--runs-json", default="")
     ap.add_argument("--no-graph", action="store_true",
-                    help="skip the HIP-graph replay of the step (reported as context)")
+                    help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--static-scale", type=float, default=None,
                     help="quantize activations with this one static fp16 scale "
                          "(w4a8_quant_act_static) instead of per-token scales")
@@ -192,8 +197,7 @@ def main():
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
     if args.print_source_hash:
-        for files in (["skinny.hip", "gemm_common.h", "quant_common.h"],
-                      ["tiled.hip", "gemm_common.h", "quant_common.h"]):
+        for files in (SKINNY_SOURCES, TILED_SOURCES):
             print(" + ".join(files), source_hash(files))
         return
 
@@ -287,10 +291,10 @@ def main():
     def new_events():
         return [(HipEvent(), HipEvent()) for _ in range(nr)]
 
-    # Timed region: `steps` steps enqueued from the host behind a GPU spin
-    # kernel, so that the whole region is already queued when the GPU reaches
-    # it and the host's launch rate never starves the GPU.  Events recorded on
-    # the launch stream around each GEMM give its on-GPU duration.
+    # Pass 1 (per-launch durations for the roofline): `steps` eager steps
+    # enqueued from the host behind a GPU spin kernel, so that the whole
+    # region is queued when the GPU reaches it; events recorded on the launch
+    # stream around each GEMM launch give its on-GPU duration.
     events = [new_events() for _ in range(args.steps)]
     for i in range(args.warmup):
         launch_step(pool[i % ncopies])
@@ -306,38 +310,43 @@ def main():
     enqueue_s = time.perf_counter() - wall0
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step_eager = total_ms / args.steps
     per_step_gemm = [[events[i][r][0].elapsed_time(events[i][r][1]) for r in range(nr)]
                      for i in range(args.steps)]
-    log(f"host enqueue {enqueue_s * 1e3:.1f} ms, GPU spin ~{spin_s * 1e3:.0f} ms, "
+    log(f"eager pass: host enqueue {enqueue_s * 1e3:.1f} ms, GPU spin ~{spin_s * 1e3:.0f} ms, "
         f"timed GPU region {total_ms:.2f} ms")
     if enqueue_s * 1e3 > total_ms + 1e3 * spin_s:
         log("warning: the host enqueue outlasted the GPU spin; the GPU may have idled")
 
-    # Context: the same steps replayed as HIP graphs (no events, no host
-    # launches in between), one graph per weight copy.
-    ms_per_step_graph = None
+    # Pass 2 (the timed steps): each step captured once as a HIP graph (one
+    # graph per weight copy of the rotation pool) and replayed, as a serving
+    # loop runs its decode steps; `steps` replays are timed between two
+    # synchronizations, enqueued behind a GPU spin.
+    ms_per_step, timing = ms_per_step_eager, "eager launches"
     if not args.no_graph:
         try:
             graphs = []
             for i in range(ncopies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
                     launch_step(pool[i])
-                graphs.append(g)
+                graphs.append(gr)
             for i in range(args.warmup):
                 graphs[i % ncopies].replay()
             torch.cuda.synchronize()
             g0 = torch.cuda.Event(enable_timing=True)
             g1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(2.4e9 * spin_s))
             g0.record()
             for i in range(args.steps):
                 graphs[i % ncopies].replay()
             g1.record()
             torch.cuda.synchronize()
-            ms_per_step_graph = g0.elapsed_time(g1) / args.steps
+            ms_per_step = g0.elapsed_time(g1) / args.steps
+            timing = "HIP graph replay of each step"
         except Exception as e:
-            log(f"graph replay unavailable: {e}")
+            log(f"graph replay unavailable ({e}); timing eager launches")
+    log(f"ms per step: {ms_per_step:.4f} ({timing}); eager {ms_per_step_eager:.4f}")
 
     gemm_us = np.array(per_step_gemm) * 1e3
     med_us = np.median(gemm_us, axis=0)
@@ -412,13 +421,13 @@ def main():
                                  "static per-tensor %g" % args.static_scale
                                  if args.static_scale is not None else "per-token dynamic"),
             "weight_rotation_copies": ncopies,
-            "launch": "host-enqueued behind a GPU spin, events around every GEMM",
+            "timing": timing,
+            "launch_durations": "separate eager pass, HIP events around every GEMM launch",
             "parallelism": "single GPU",
         },
         "tops": round(value_tops, 3),
         "gbps": round(value_gbs, 2),
-        "ms_per_step_graph_replay": (round(ms_per_step_graph, 4)
-                                     if ms_per_step_graph is not None else None),
+        "ms_per_step_eager": round(ms_per_step_eager, 4),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
     }

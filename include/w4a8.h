@@ -180,7 +180,9 @@ typedef struct {
   int slices;    /* tiled: workgroups that split K of one tile (1..16), their
                     int32 partial sums going through the workspace, which
                     must then hold slices * m * n * 4 bytes; 0 = auto */
-  int reserved;
+  int workgroups;/* w4a8_linear's fused kernel: workgroups of its persistent
+                    grid, each walking column-tile groups (1 .. the number of
+                    groups; larger values are clamped), 0 = auto */
 } w4a8_gemm_opts;
 
 /* Workspace bytes w4a8_gemm needs for these arguments (0 when it needs none,
@@ -196,12 +198,15 @@ w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
 /* ------------------------------------------------------------ whole layer
  * The W4A8 linear layer from fp16 activations: per-token quantization of A
  * (as w4a8_quant_act) followed by the GEMM (as w4a8_gemm), with A8 and s_a
- * written to a8_dev / s_a_dev as well.  For 1 or 2 tokens both steps run
- * in one kernel: every workgroup quantizes the rows itself while its first
- * weight loads are in flight, which saves a launch and a round trip of A8
- * through memory; otherwise it makes the two calls in order on `stream`.
- * (opts->variant = 3 forces the fused kernel for up to 8 tokens, when each
- * workgroup's int8 copy of its rows fits in 96 KiB of LDS.)
+ * written to a8_dev / s_a_dev as well.  For fewer than 32768 activations
+ * (m * k; e.g. up to 4 tokens at k = 4096) both steps run in one kernel:
+ * each workgroup of a persistent grid quantizes the rows itself while its
+ * first weight loads are in flight, then walks several column tiles, which
+ * saves a launch and a round trip of A8 through memory; otherwise it makes
+ * the two calls in order on `stream`.  (opts->variant = 3 forces the fused
+ * kernel for up to 16 tokens, when m rounded up to a power of two times the
+ * 128-k blocks of each wave's K range is at most 64, each wave's range at
+ * most 16 blocks; opts->workgroups sets its grid.)
  * Outputs are bit-identical either way (Y to the last bit: the same int32
  * sums, scales and epilogue).
  *   a_dev     m x k fp16, row stride lda elements (lda >= k, lda % 8 == 0,

@@ -303,24 +303,42 @@ def test_linear_validates_before_any_hip_call():
     opts = w4.GemmOpts(4)
     assert call(opts=ctypes.byref(opts)) == 1          # no such variant
     opts = w4.GemmOpts(3)
-    assert call(m=9, opts=ctypes.byref(opts)) == 2     # fused: at most 8 rows
+    assert call(m=17, opts=ctypes.byref(opts)) == 2    # fused: at most 16 rows
+    assert call(m=8, k=14336, lda=14336, lda8=14336, opts=ctypes.byref(opts)) == 2  # rows x K range
+    opts = w4.GemmOpts(3, 0, 0, 0, 0, 0, 0, -1)
+    assert call(opts=ctypes.byref(opts)) == 1          # negative workgroup count
+    opts = w4.GemmOpts(3)
     assert call(m=4, k=131072, lda=131072, lda8=131072, opts=ctypes.byref(opts)) == 2  # long K
 
 
 def test_linear_launch_plan():
-    """w4a8_linear_launches: one fused launch for 1-2 tokens (LDS permitting),
-    two otherwise, three when the GEMM splits K over workgroups."""
+    """w4a8_linear_launches: one fused launch below 32768 activations
+    (M x K) where the fused kernel applies, two otherwise, three when the
+    GEMM splits K over workgroups; forced, the fused kernel takes up to 16
+    tokens (rows x k-blocks per wave within its budget, wave ranges of at
+    most 16 blocks)."""
     L = w4.lib
     assert L.w4a8_linear_launches(1, 4096, 4096, 128, None) == 1
     assert L.w4a8_linear_launches(2, 28672, 4096, 32, None) == 1
     assert L.w4a8_linear_launches(1, 4096, 14336, 0, None) == 1
-    assert L.w4a8_linear_launches(3, 4096, 4096, 128, None) == 2
-    assert L.w4a8_linear_launches(16, 4096, 14336, 128, None) == 2
+    assert L.w4a8_linear_launches(4, 4096, 4096, 128, None) == 1
+    assert L.w4a8_linear_launches(2, 4096, 14336, 128, None) == 1
+    assert L.w4a8_linear_launches(2, 256, 1024, 1, None) == 1         # codebook weights
+    assert L.w4a8_linear_launches(8, 4096, 4096, 128, None) == 2      # 32768 activations
+    assert L.w4a8_linear_launches(4, 4096, 14336, 128, None) == 2
+    assert L.w4a8_linear_launches(16, 4096, 4096, 128, None) == 2
+    assert L.w4a8_linear_launches(17, 4096, 4096, 128, None) == 2
     assert L.w4a8_linear_launches(256, 4096, 14336, 128, None) == 3
     assert L.w4a8_linear_launches(1, 4096, 131072, 128, None) == 2    # K range too long to fuse
     opts = w4.GemmOpts(3)
-    assert L.w4a8_linear_launches(8, 4096, 4096, 128, ctypes.byref(opts)) == 1
-    assert L.w4a8_linear_launches(9, 4096, 4096, 128, ctypes.byref(opts)) == 0
+    assert L.w4a8_linear_launches(16, 4096, 4096, 128, ctypes.byref(opts)) == 1
+    assert L.w4a8_linear_launches(4, 4096, 14336, 128, ctypes.byref(opts)) == 1
+    assert L.w4a8_linear_launches(5, 4096, 14336, 128, ctypes.byref(opts)) == 0  # 8 rows x 16 blocks
+    assert L.w4a8_linear_launches(17, 4096, 4096, 128, ctypes.byref(opts)) == 0
+    opts = w4.GemmOpts(3, 0, 4)
+    assert L.w4a8_linear_launches(1, 4096, 4096, 128, ctypes.byref(opts)) == 0  # 1 or 2 tiles
+    opts = w4.GemmOpts(3, 0, 0, 0, 0, 0, 0, -1)
+    assert L.w4a8_linear_launches(1, 4096, 4096, 128, ctypes.byref(opts)) == 0
     assert L.w4a8_linear_launches(1, 4008, 4096, 128, None) == 0      # n % 16
 
 

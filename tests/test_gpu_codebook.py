@@ -45,21 +45,24 @@ def test_codebook_every_kernel_shape():
         assert np.array_equal(acc, out["acc"][:mm])
 
 
-def test_codebook_linear_two_launches():
-    """w4a8_linear in the codebook mode (quantizer + GEMM: no fused kernel)."""
+@pytest.mark.parametrize("m,launches", [(2, 1), (30, 2)])
+def test_codebook_linear(m, launches):
+    """w4a8_linear in the codebook mode: the fused kernel for a few tokens,
+    quantizer + GEMM for more."""
     import torch
     dev = device()
-    m, n, k = 2, 256, 1024
+    n, k = 256, 1024
     w = synth.weights(n, k, seed=8)
     a = synth.activations(m, k, seed=9)
     out = ref.linear(a, w, NF)
-    assert w4.lib.w4a8_linear_launches(m, n, k, NF, None) == 2
-    log("codebook linear")
+    assert w4.lib.w4a8_linear_launches(m, n, k, NF, None) == launches
+    log(f"codebook linear m={m}")
     y, a8, s_a, acc = w4.linear(torch.from_numpy(a).to(dev), w4.to_device(w4.pack(w, NF), dev),
                                 n, k, NF, want_acc=True)
     torch.cuda.synchronize()
     assert np.array_equal(a8.cpu().numpy(), out["a8"])
     assert np.array_equal(acc.cpu().numpy(), out["acc"])
+    assert ref.y_tolerance_ok(y.cpu().numpy(), out["y"]).all()
 
 
 @pytest.mark.parametrize("m", [1, 16, 1024])

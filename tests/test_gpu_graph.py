@@ -39,3 +39,43 @@ def test_graph_replays_match_eager(m, n, k, g):
         torch.cuda.synchronize()
         assert torch.equal(acc, acc_ref)
         assert torch.equal(y, y_ref)
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 4096, 4096, 128), (2, 6144, 4096, 32), (4, 4096, 14336, 128),
+                                     (256, 4096, 14336, 128), (64, 512, 1024, 1)])
+def test_graph_whole_layer_replays_match_eager(m, n, k, g):
+    """w4a8_linear (fused for 1-2 tokens, quantizer + GEMM otherwise, K split
+    through a workspace at M = 256, codebook weights) inside a captured graph:
+    every replay, with eager work and synchronizations in between, equals
+    the eager result."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = synth.weights(n, k, seed=17)
+    wdev = w4.to_device(w4.pack(w, g), dev)
+    a = torch.from_numpy(synth.activations(m, k, seed=18)).to(dev)
+    a8 = torch.empty((m, k), dtype=torch.int8, device=dev)
+    s_a = torch.empty((m,), dtype=torch.float16, device=dev)
+    y = torch.empty((m, n), dtype=torch.float16, device=dev)
+    acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    ws_bytes = int(w4.lib.w4a8_gemm_workspace_size(m, n, k, g, None))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    log(f"graph linear m={m} n={n} k={k} g={g}: eager (launches "
+        f"{w4.lib.w4a8_linear_launches(m, n, k, g, None)})")
+    w4.linear(a, wdev, n, k, g, y=y, a8=a8, s_a=s_a, acc=acc, workspace=ws)
+    torch.cuda.synchronize()
+    y_ref, acc_ref, a8_ref = y.clone(), acc.clone(), a8.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        w4.linear(a, wdev, n, k, g, y=y, a8=a8, s_a=s_a, acc=acc, workspace=ws)
+    for rep in range(4):
+        y.fill_(0)
+        acc.fill_(0)
+        a8.fill_(0)
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        log(f"graph linear m={m} n={n} k={k} g={g}: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(acc, acc_ref)
+        assert torch.equal(y, y_ref)
+        assert torch.equal(a8, a8_ref)

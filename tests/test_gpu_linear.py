@@ -3,6 +3,8 @@ into the small-M GEMM, against the CPU oracle and against the two-launch path.
 
 Bar: A8, s_a and the int32 accumulators bit-exact with the oracle; Y within
 the oracle tolerance and bit-identical to quantizer + GEMM."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -50,15 +52,24 @@ SHAPES = [  # n, k, g
 ]
 
 
+def _fused_applies(m, n, k, g, **opts):
+    o = w4.GemmOpts(3, opts.get("k_split", 0), opts.get("n_tiles", 0), 0, 0, 0, 0,
+                    opts.get("workgroups", 0))
+    return int(w4.lib.w4a8_linear_launches(m, n, k, g, ctypes.byref(o))) == 1
+
+
 @pytest.mark.parametrize("n,k,g", SHAPES)
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 12, 16])
 def test_linear_fused_matches_oracle_and_two_launches(m, n, k, g):
+    """Where the fused kernel applies (rows x blocks per wave within its
+    register budget) it is forced; elsewhere the automatic path runs."""
     w = synth.weights(n, k, seed=500 + n + k + g, dist="student_t4")
     a = synth.activations(m, k, seed=600 + m + k)
     out = ref.linear(a, w, g)
     blob = w4.pack(w, g)
-    log(f"linear fused m={m} n={n} k={k} g={g}")
-    y, a8, s_a, acc = _run_linear(a, blob, n, k, g, variant=3)
+    fused = _fused_applies(m, n, k, g)
+    log(f"linear {'fused' if fused else 'auto'} m={m} n={n} k={k} g={g}")
+    y, a8, s_a, acc = _run_linear(a, blob, n, k, g, variant=3 if fused else 0)
     assert np.array_equal(s_a.view(np.uint16), out["s_a"].view(np.uint16))
     assert np.array_equal(a8, out["a8"])
     assert np.array_equal(acc, out["acc"])
@@ -69,18 +80,63 @@ def test_linear_fused_matches_oracle_and_two_launches(m, n, k, g):
     assert np.array_equal(y2.view(np.uint16), y.view(np.uint16))
 
 
-@pytest.mark.parametrize("n_tiles,k_split", [(1, 1), (1, 8), (2, 3), (4, 2), (4, 8), (2, 5)])
-def test_linear_fused_every_shape(n_tiles, k_split):
+@pytest.mark.parametrize("n_tiles,k_split,workgroups", [
+    (1, 1, 0), (1, 8, 0), (2, 3, 0), (2, 5, 0), (2, 2, 0),
+    (1, 8, 1), (2, 2, 3), (1, 4, 7), (2, 8, 2), (2, 1, 10), (1, 2, 64)])
+def test_linear_fused_every_shape(n_tiles, k_split, workgroups):
+    """Every column-tile count, K split (including waves without blocks) and
+    persistent grid (one workgroup for all groups, ragged group counts per
+    workgroup, more workgroups than groups) gives the oracle's result."""
     n, k, g, m = 320, 2048, 32, 4
     w = synth.weights(n, k, seed=71, dist="student_t4")
     a = synth.activations(m, k, seed=72)
     out = ref.linear(a, w, g)
-    log(f"linear fused n_tiles={n_tiles} k_split={k_split}")
+    log(f"linear fused n_tiles={n_tiles} k_split={k_split} workgroups={workgroups}")
     y, a8, s_a, acc = _run_linear(a, w4.pack(w, g), n, k, g, variant=3, n_tiles=n_tiles,
-                                  k_split=k_split)
+                                  k_split=k_split, workgroups=workgroups)
     assert np.array_equal(a8, out["a8"])
     assert np.array_equal(acc, out["acc"])
     assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
+@pytest.mark.parametrize("m,n,k,g,workgroups", [
+    (16, 4112, 4096, 128, 0), (16, 4112, 4096, 128, 100), (11, 1040, 4096, 64, 7),
+    (4, 4096, 14336, 128, 0), (8, 2064, 8192, 128, 50), (13, 272, 2048, 1, 3),
+    (2, 6144, 4096, 1, 0)])
+def test_linear_fused_up_to_16_rows(m, n, k, g, workgroups):
+    """Up to 16 tokens, long wave ranges (16 blocks), codebook weights, and
+    persistent grids: A8, s_a and acc bit-exact with the oracle."""
+    w = synth.weights(n, k, seed=131 + m, dist="student_t4")
+    a = synth.activations(m, k, seed=132 + m)
+    assert _fused_applies(m, n, k, g, workgroups=workgroups)
+    out = ref.linear(a, w, g)
+    log(f"linear fused m={m} n={n} k={k} g={g} workgroups={workgroups}")
+    y, a8, s_a, acc = _run_linear(a, w4.pack(w, g), n, k, g, variant=3, workgroups=workgroups)
+    assert np.array_equal(s_a.view(np.uint16), out["s_a"].view(np.uint16))
+    assert np.array_equal(a8, out["a8"])
+    assert np.array_equal(acc, out["acc"])
+    assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
+def test_linear_fused_rounding_ties():
+    """Rows built so that A * (1 / s_a) lands on every half-integer and near
+    the clamp: s_a = 1 (absmax 127), 2 (absmax 254) and an inexact scale."""
+    n, k, g = 64, 2048, 128
+    rng = np.random.default_rng(141)
+    rows = []
+    for amax in (127.0, 254.0, 100.0, 1000.0):
+        halves = np.arange(-2 * amax, 2 * amax + 1) / 2.0            # every multiple of 0.5
+        row = rng.choice(halves, size=k).astype(np.float16)
+        row[rng.integers(k)] = np.float16(amax)
+        rows.append(row)
+    a = np.stack(rows)
+    w = synth.weights(n, k, seed=142)
+    out = ref.linear(a, w, g)
+    log("linear fused rounding ties")
+    y, a8, s_a, acc = _run_linear(a, w4.pack(w, g), n, k, g, variant=3)
+    assert np.array_equal(s_a.view(np.uint16), out["s_a"].view(np.uint16))
+    assert np.array_equal(a8, out["a8"])
+    assert np.array_equal(acc, out["acc"])
 
 
 def test_linear_strided_rows_and_padding():
@@ -96,11 +152,13 @@ def test_linear_strided_rows_and_padding():
     assert np.array_equal(acc, out["acc"])
 
 
-@pytest.mark.parametrize("m,n,k,g", [(16, 256, 14336, 128), (9, 64, 512, 128), (100, 272, 768, 64),
+@pytest.mark.parametrize("m,n,k,g", [(16, 256, 14336, 128), (17, 64, 512, 128), (100, 272, 768, 64),
                                      (4, 64, 131072, 128)])
 def test_linear_two_launch_path(m, n, k, g):
-    """Where the fused kernel does not apply (more than 8 rows, or its LDS
-    copy of A would not fit), the same call runs quantizer + GEMM."""
+    """Where the fused kernel does not apply (more than 16 rows, rows x
+    blocks per wave beyond its register budget, or a wave range longer than
+    16 blocks), the same call runs quantizer + GEMM."""
+    assert not _fused_applies(m, n, k, g)
     w = synth.weights(n, k, seed=91 + m)
     a = synth.activations(m, k, seed=92 + m)
     blob = w4.pack(w, g)

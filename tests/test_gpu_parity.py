@@ -42,6 +42,28 @@ def test_quant_act_exhaustive_fp16_scales():
     assert np.array_equal(a8, want_a8)
 
 
+def test_quant_act_every_fp16_value():
+    """Every finite fp16 value quantized under five scales (s_a = 1, 2, 0.5,
+    an inexact one and the largest), so that A * (1 / s_a) meets every
+    half-integer tie and the clamp: A8 bit-exact."""
+    vals = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    vals = vals[np.isfinite(vals)]
+    rows = []
+    for amax in (127.0, 254.0, 63.5, 100.0, 65504.0):
+        row = vals[np.abs(vals.astype(np.float32)) <= amax]
+        row = np.concatenate([row, [np.float16(amax)]])
+        rows.append(row)
+    k = max(r.size for r in rows)
+    a = np.zeros((len(rows), k), dtype=np.float16)
+    for i, r in enumerate(rows):
+        a[i, :r.size] = r
+    log(f"quant_act every fp16 value m={a.shape[0]} k={k}")
+    a8, s_a = run_quant_act(a)
+    want_a8, want_sa = ref.quant_act(a)
+    assert np.array_equal(s_a.view(np.uint16), want_sa.view(np.uint16))
+    assert np.array_equal(a8, want_a8)
+
+
 def test_quant_act_zero_rows_and_ties():
     a = np.zeros((4, 256), dtype=np.float16)
     a[1, :8] = [127, 2.5, -3.5, 0.5, -0.5, 1.5, 0, -127]

@@ -49,7 +49,7 @@ class GemmOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("k_split", ctypes.c_int),
                 ("n_tiles", ctypes.c_int), ("m_tiles", ctypes.c_int),
                 ("stages", ctypes.c_int), ("row_groups", ctypes.c_int),
-                ("slices", ctypes.c_int), ("reserved", ctypes.c_int)]
+                ("slices", ctypes.c_int), ("workgroups", ctypes.c_int)]
 
 
 def _load():
@@ -233,7 +233,7 @@ def gemm(a8, s_a, blob_dev, n: int, k: int, g: int, y=None, acc=None, want_acc=F
 def linear(a, blob_dev, n: int, k: int, g: int, y=None, a8=None, s_a=None, acc=None,
            want_acc=False, variant: int = 0, k_split: int = 0, n_tiles: int = 0,
            m_tiles: int = 0, stages: int = 0, row_groups: int = 0, slices: int = 0,
-           workspace=None, stream=None):
+           workgroups: int = 0, workspace=None, stream=None):
     """The whole layer from fp16 activations (fused for small M); returns
     (y, a8, s_a) or (y, a8, s_a, acc)."""
     torch = _torch()
@@ -248,8 +248,8 @@ def linear(a, blob_dev, n: int, k: int, g: int, y=None, a8=None, s_a=None, acc=N
     if want_acc and acc is None:
         acc = torch.empty((m, n), dtype=torch.int32, device=a.device)
     opts = None
-    if variant or k_split or n_tiles or m_tiles or stages or row_groups or slices:
-        opts = GemmOpts(variant, k_split, n_tiles, m_tiles, stages, row_groups, slices)
+    if variant or k_split or n_tiles or m_tiles or stages or row_groups or slices or workgroups:
+        opts = GemmOpts(variant, k_split, n_tiles, m_tiles, stages, row_groups, slices, workgroups)
     ws_opts = opts if (opts is None or variant != 3) else None
     ws_need = 0 if variant == 3 else int(lib.w4a8_gemm_workspace_size(
         m, n, k, g, ctypes.byref(ws_opts) if ws_opts is not None else None))

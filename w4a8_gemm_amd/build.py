@@ -8,6 +8,7 @@ quantization is a single IEEE operation.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -44,18 +45,22 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for src in ("skinny.hip", "tiled.hip", "quant_act.hip", "w4a16.hip"):
+    steps = []
+    for src in ("fused.hip", "skinny.hip", "tiled.hip", "quant_act.hip", "w4a16.hip"):
         obj = os.path.join(BUILD, src + ".o")
-        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        steps.append((obj, [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
     obj = os.path.join(BUILD, "api.cpp.o")
-    _run([HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "api.cpp"), "-o", obj], verbose)
-    objs.append(obj)
+    steps.append((obj, [HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "api.cpp"),
+                        "-o", obj]))
     gxx = shutil.which("g++") or "g++"
     obj = os.path.join(BUILD, "pack.cpp.o")
-    _run([gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "pack.cpp"), "-o", obj], verbose)
-    objs.append(obj)
+    steps.append((obj, [gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "pack.cpp"), "-o", obj]))
+    # the compilations are independent processes: run them side by side
+    workers = max(1, min(len(steps), os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for _, cmd in steps]:
+            f.result()
+    objs = [obj for obj, _ in steps]
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-pthread"], verbose)
     os.replace(tmp, LIB)

@@ -254,25 +254,29 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
 
 namespace {
 
-// Skinny configuration for the fused kernel: the automatic skinny choice
-// with one row tile, at most 2 column tiles per wave above 4 rows, and each
-// wave's K range at most 16 blocks; forced options as for w4a8_gemm.
+// Configuration of the fused kernel: one row tile; one column tile per
+// group for narrow layers (<= 256 tiles), else two; K split over up to 8
+// waves with 4, 8 or 16 blocks each (every wave kept, as for the skinny
+// kernel); a persistent grid of kFusedAutoWgs workgroups unless forced.
 SkinnyConfig fused_plan(int m, int n, int k, const w4a8_gemm_opts* opts) {
-  SkinnyConfig c = choose_skinny(m, n, k);
+  (void)m;
+  SkinnyConfig c{};
   c.mr = 1;
-  if (m > 4 && c.nc > 2) {
-    c.nc = 2;
-    c.kw = std::min(8, std::max(1, (k / kKBlock) / 4));
-    c.kbw = blocks_per_wave(k / kKBlock, c.kw);
-    c.kw = (k / kKBlock + c.kbw - 1) / c.kbw;
-  }
+  const int kblocks = k / kKBlock;
+  c.nc = n / kColTile <= 256 ? 1 : 2;
+  c.kw = std::min(8, std::max(1, kblocks / 4));
+  if (opts && opts->k_split > 0) c.kw = opts->k_split;
+  const int per = (kblocks + c.kw - 1) / c.kw;
+  c.kbw = per <= 4 ? 4 : (per <= 8 ? 8 : (per <= 16 ? 16 : 0));
   if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
-  if (opts && opts->k_split > 0) {
-    c.kw = opts->k_split;
-    c.kbw = blocks_per_wave(k / kKBlock, c.kw);
-  }
+  c.wgs = kFusedAutoWgs;
+  if (opts && opts->workgroups != 0) c.wgs = opts->workgroups;
   return c;
 }
+
+// The automatic choice runs the fused kernel wherever it applies for fewer
+// than kFusedAutoElems activations.
+bool fused_by_default(int m, int k) { return long(m) * k < kFusedAutoElems; }
 
 }  // namespace
 
@@ -290,13 +294,14 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
   if (!aligned16(a_dev) || !aligned16(a8_dev) || !aligned16(blob_dev))
     return W4A8_ERR_INVALID_ARGUMENT;
   const int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant > 3) return W4A8_ERR_INVALID_ARGUMENT;
+  if (variant < 0 || variant > 3 || (opts && opts->workgroups < 0))
+    return W4A8_ERR_INVALID_ARGUMENT;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const SkinnyConfig fc = fused_plan(m, n, k, opts);
-  const bool fused_ok = g != W4A8_CODEBOOK_NF && fused_config_supported(fc, m, k);
+  const bool fused_ok = fused_config_supported(fc, m, k);
   if (variant == 3 && !fused_ok) return W4A8_ERR_UNSUPPORTED;
-  if (variant == 3 || (variant == 0 && fused_ok && m <= kFusedAutoRows)) {
+  if (variant == 3 || (variant == 0 && fused_ok && fused_by_default(m, k))) {
     Sections sec = sections(n, k, g);
     const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
     GemmParams p{};
@@ -369,11 +374,10 @@ extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
 extern "C" int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_opts* opts) {
   if (m <= 0 || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
   const int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant > 3) return 0;
-  const bool fused_ok =
-      g != W4A8_CODEBOOK_NF && fused_config_supported(fused_plan(m, n, k, opts), m, k);
+  if (variant < 0 || variant > 3 || (opts && opts->workgroups < 0)) return 0;
+  const bool fused_ok = fused_config_supported(fused_plan(m, n, k, opts), m, k);
   if (variant == 3) return fused_ok ? 1 : 0;
-  if (variant == 0 && fused_ok && m <= kFusedAutoRows) return 1;
+  if (variant == 0 && fused_ok && fused_by_default(m, k)) return 1;
   return plan_gemm(m, n, k, opts).slices > 1 ? 3 : 2;
 }
 

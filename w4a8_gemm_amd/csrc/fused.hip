@@ -1,0 +1,347 @@
+// W4A8 linear layer for gfx950 with the per-token activation quantization
+// fused into the small-M GEMM: one launch instead of quantizer + GEMM.
+//
+// The quantization needs each token's largest |A| over all of K before any
+// int8 operand exists, and every workgroup multiplies all of K, so every
+// workgroup quantizes all M x K activations itself (the standalone quantizer
+// does it once for the whole GPU).  That costs vector-ALU time per
+// workgroup, so the grid is persistent: about one workgroup per compute unit,
+// each walking column-tile groups blockIdx.x, blockIdx.x + gridDim.x, ...,
+// quantizes A once and reuses the int8 rows for all its tiles.
+//
+// Workgroup = kw waves splitting K (wave wk owns the 128-k blocks
+// [wk * KBW, (wk + 1) * KBW)), one 16-row tile (M <= 16), NC 16-column tiles
+// per group.  Partial int32 tiles of the waves are summed exactly through LDS.
+//
+// Prologue: each wave loads its K range of rows 0 .. M-1 (fp16, 16-byte
+// chunks spread over all 64 lanes) into registers; the weight ring of the
+// first tile group is issued right behind those loads, so the weight stream
+// starts at once.  The waves' partial row maxima meet in LDS; every wave
+// derives s_a and fp32(1 / s_a) as the standalone quantizer does (the same
+// device functions, so the same bits) and writes its int8 rows to its LDS
+// slab, from which the K loop reads the MFMA A operands.  Workgroup 0 also
+// stores A8 and s_a.
+//
+// Weight ring: slot j = v % D holds block v of the wave's range; once block
+// v has been multiplied the slot is refilled with block v + D, which past the
+// end of the range is block v + D - KBW of the next tile group, so the
+// stream does not drain between groups.  Blocks past the wave's real range
+// (the last wave, when K does not fill kw * KBW blocks) are loaded clamped to
+// its last real block (a cache hit) and not multiplied.
+//
+// LDS: [kw][16] uint32 row maxima, [16] float s_a, [2][kw][NC][256] int32
+// partial tiles when kw > 1 (the halves alternate between tile groups, so one
+// barrier per group suffices), then [kw][M][slab] int8 rows with
+// slab = KBW * 128 + 16 bytes (the pad staggers rows over the banks).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace w4a8 {
+namespace {
+
+using namespace dev;
+
+template <int NC, int GPB, int D, int MF, int KBW>
+__global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t* a, int lda) {
+  static_assert(KBW % D == 0, "ring groups must tile the wave's range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int CPL = KBW / 4;   // 16-byte fp16 chunks per lane and row
+  const int lane = threadIdx.x & 63;
+  const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = blockDim.x >> 6;
+  const int quarter = lane >> 4;
+  const int r16 = lane & 15;
+
+  const int ntiles = p.n >> 4;
+  const int ngroups = (ntiles + NC - 1) / NC;
+  const int kblocks = p.k >> 7;
+  const int kb_begin = min(kblocks, wk * KBW);
+  const int nreal = min(kblocks - kb_begin, KBW);            // may be 0
+  const int kb_last = min(kblocks - 1, kb_begin + max(nreal, 1) - 1);
+  constexpr int slab = KBW * 128 + 16;
+
+  uint32_t* amax_lds = reinterpret_cast<uint32_t*>(lds);
+  float* sa_lds = reinterpret_cast<float*>(lds + kw * 64);
+  int32_t* red = reinterpret_cast<int32_t*>(lds + kw * 64 + 64);
+  const int red_bytes = kw > 1 ? 2 * kw * NC * 1024 : 0;
+  int8_t* my_slab = reinterpret_cast<int8_t*>(lds + kw * 64 + 64 + red_bytes) + wk * p.m * slab;
+
+  constexpr int MSTEP = GPB <= 0 ? D : 4 / GPB;   // ring slots per meta dword
+  u32x4 q[D][NC];
+  uint32_t md[D][NC], mdn[D][NC];
+  // load block vv of the wave's range, column-tile group tg, into slot j
+  auto issue = [&](int j, int tg, int vv) {
+    const int kb = min(kb_begin + vv, kb_last);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int t = min(tg * NC + c, ntiles - 1);
+      q[j][c] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(p.q + ((size_t(t) * kblocks + kb) * 64 + lane) * 16));
+    }
+    if (GPB >= 0 && j % MSTEP == 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int t = min(tg * NC + c, ntiles - 1);
+        const uint32_t* mrow =
+            reinterpret_cast<const uint32_t*>(p.meta + size_t(t * 16 + r16) * p.meta_row_bytes);
+        mdn[j][c] = mrow[GPB == 0 ? 0 : (kb * GPB) >> 2];
+      }
+    }
+  };
+  auto next_group_meta = [&]() {
+    if (GPB < 0) return;
+#pragma unroll
+    for (int j = 0; j < D; j += MSTEP)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) md[j][c] = mdn[j][c];
+  };
+
+  // ---- quantization prologue.  The activation loads go out first and the
+  // weight ring right behind them: vector-memory counters complete in order,
+  // so waiting for the activations does not wait for the weights.
+  const int k0 = kb_begin * 128;
+  const int cpr = nreal * 16;   // chunks per row in the wave's range
+  uint4 chunk[MF][CPL];
+#pragma unroll
+  for (int r = 0; r < MF; ++r) {
+    const uint16_t* src = a + size_t(min(r, p.m - 1)) * lda + k0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = j * 64 + lane;
+      chunk[r][j] = (r < p.m && c < cpr) ? *reinterpret_cast<const uint4*>(src + c * 8)
+                                         : uint4{0, 0, 0, 0};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int tg0 = blockIdx.x;
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue(j, tg0, j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < MF; ++r) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) mx = absmax8(mx, chunk[r][j]);
+    uint32_t m16 = absmax_bits(mx);
+    for (int off = 32; off > 0; off >>= 1) m16 = max(m16, uint32_t(__shfl_xor(int(m16), off)));
+    if (lane == 0) amax_lds[wk * 16 + r] = m16;
+  }
+  __syncthreads();
+  const bool store_a8 = blockIdx.x == 0;
+#pragma unroll
+  for (int r = 0; r < MF; ++r) {
+    if (r >= p.m) continue;   // (not break: the loop must stay unrolled)
+    uint32_t am = 0;
+    for (int w = 0; w < kw; ++w) am = max(am, amax_lds[w * 16 + r]);
+    const uint16_t sb = act_scale_bits(am);
+    const float rc = act_recip(sb);
+    if (wk == 0 && lane == 0) {
+      sa_lds[r] = h2f(sb);
+      if (store_a8) p.s_a_out[r] = sb;
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = j * 64 + lane;
+      if (c < cpr) {
+        const uint2 o = quant8(chunk[r][j], rc);
+        *reinterpret_cast<uint2*>(my_slab + r * slab + c * 8) = o;
+        if (store_a8) *reinterpret_cast<uint2*>(p.a8_out + size_t(r) * p.lda8 + k0 + c * 8) = o;
+      }
+    }
+  }
+  __syncthreads();   // slabs and s_a visible (each wave reads only its own slab)
+
+  float sa[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sa[r] = sa_lds[min(4 * quarter + r, p.m - 1)];
+
+  // A operand of lane (row r16, k quarter) for block v, half h; rows past M
+  // read row M - 1 (their products are never stored)
+  const int8_t* arow = my_slab + min(r16, p.m - 1) * slab + 16 * quarter;
+  v4i acc[NC];
+
+  // decode block v from ring slot j = v % D and multiply it into acc
+  auto compute = [&](int j, int v) {
+    const u32x4 (&qs)[NC] = q[j];
+    const uint32_t (&ms)[NC] = md[j - j % MSTEP];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i af = *reinterpret_cast<const v4i*>(arow + v * 128 + 64 * h);
+      // byte of this lane's group in the meta dword (kb_begin % 4 == 0)
+      int byte = 0;
+      if (GPB == 1) byte = v & 3;
+      if (GPB == 2) byte = 2 * (v & 1) + h;
+      if (GPB == 4) byte = 2 * h + (quarter >> 1);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t w0 = h ? qs[c].z : qs[c].x;
+        const uint32_t w1 = h ? qs[c].w : qs[c].y;
+        v4i bf;
+        if constexpr (GPB < 0) {
+          bf = decode16_lut(w0, w1);
+        } else {
+          bf = decode16(w0, w1, group_const((ms[c] >> (8 * byte)) & 0xFFu));
+        }
+        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[c], 0, 0, 0);
+      }
+    }
+  };
+
+  // One column-tile group: K loop, then the split-K sum and the epilogue.
+  // With HAS_NEXT the ring slots freed by the last D blocks are refilled
+  // from the next group; the workgroup's last group issues no such loads.
+  // The two copies keep every load unconditional inside the unrolled loop.
+  auto run_group = [&](int tg, int tg_next, int it, auto has_next) {
+    constexpr bool HAS_NEXT = decltype(has_next)::value;
+    float s1[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) s1[c] = h2f(p.s1[min((tg * NC + c) * 16 + r16, p.n - 1)]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < KBW; ++v) {
+      const int j = v % D;
+      if (v < nreal) compute(j, v);
+      if (v + D < KBW) issue(j, tg, v + D);
+      else if (HAS_NEXT) issue(j, tg_next, v + D - KBW);
+      if (j == D - 1) next_group_meta();
+    }
+
+    if (kw == 1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (tg * NC + c >= ntiles) continue;
+        int32_t v[4] = {acc[c][0], acc[c][1], acc[c][2], acc[c][3]};
+        store_frag(p, 0, (tg * NC + c) * 16, lane, v, s1[c], sa);
+      }
+      return;
+    }
+    int32_t* part = red + (it & 1) * kw * NC * 256;
+    int32_t* mine = part + wk * NC * 256;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mine[(c * 4 + r) * 64 + lane] = acc[c][r];
+    __syncthreads();
+    for (int c = wk; c < NC; c += kw) {
+      if (tg * NC + c >= ntiles) continue;
+      int32_t v[4] = {0, 0, 0, 0};
+      for (int w = 0; w < kw; ++w) {
+        const int32_t* pp = part + (w * NC + c) * 256;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += pp[r * 64 + lane];
+      }
+      float s1c = s1[0];
+#pragma unroll
+      for (int cc = 1; cc < NC; ++cc)
+        if (cc == c) s1c = s1[cc];
+      store_frag(p, 0, (tg * NC + c) * 16, lane, v, s1c, sa);
+    }
+  };
+
+  next_group_meta();
+  const int stride = gridDim.x;
+  int tg = tg0, it = 0;
+  for (; tg + stride < ngroups; tg += stride, ++it)
+    run_group(tg, tg + stride, it, std::true_type{});
+  run_group(tg, tg, it, std::false_type{});   // tg0 < ngroups: every workgroup has a last group
+}
+
+template <int NC, int GPB, int MF, int KBW>
+hipError_t launch_fused_t(const GemmParams& p, const uint16_t* a, int lda, const SkinnyConfig& c,
+                          hipStream_t stream) {
+  constexpr int D = 4;
+  const void* fn = reinterpret_cast<const void*>(&fused_kernel<NC, GPB, D, MF, KBW>);
+  const size_t lds = fused_lds_bytes(c.kw, NC, p.m, KBW);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  const int ngroups = (p.n / 16 + NC - 1) / NC;
+  const int grid = c.wgs > 0 ? std::min(c.wgs, ngroups) : ngroups;
+  GemmParams arg = p;
+  arg.kb_per_wave = KBW;
+  const uint16_t* a_arg = a;
+  int lda_arg = lda;
+  void* args[] = {&arg, &a_arg, &lda_arg};
+  return hipLaunchKernel(fn, dim3(grid), dim3(64 * c.kw), args, lds, stream);
+}
+
+template <int NC, int MF, int KBW>
+hipError_t fused_by_gpb(const GemmParams& p, const uint16_t* a, int lda, int gpb,
+                        const SkinnyConfig& c, hipStream_t s) {
+  switch (gpb) {
+    case -1: return launch_fused_t<NC, -1, MF, KBW>(p, a, lda, c, s);
+    case 0: return launch_fused_t<NC, 0, MF, KBW>(p, a, lda, c, s);
+    case 1: return launch_fused_t<NC, 1, MF, KBW>(p, a, lda, c, s);
+    case 2: return launch_fused_t<NC, 2, MF, KBW>(p, a, lda, c, s);
+    case 4: return launch_fused_t<NC, 4, MF, KBW>(p, a, lda, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int MF, int KBW>
+hipError_t fused_by_nc(const GemmParams& p, const uint16_t* a, int lda, int gpb,
+                       const SkinnyConfig& c, hipStream_t s) {
+  switch (c.nc) {
+    case 1: return fused_by_gpb<1, MF, KBW>(p, a, lda, gpb, c, s);
+    case 2: return fused_by_gpb<2, MF, KBW>(p, a, lda, gpb, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int MF>
+hipError_t fused_by_kbw(const GemmParams& p, const uint16_t* a, int lda, int gpb,
+                        const SkinnyConfig& c, hipStream_t s) {
+  switch (c.kbw) {
+    case 4: return fused_by_nc<MF, 4>(p, a, lda, gpb, c, s);
+    case 8:
+      if constexpr (MF * 8 <= kFusedMaxHold) return fused_by_nc<MF, 8>(p, a, lda, gpb, c, s);
+      break;
+    case 16:
+      if constexpr (MF * 16 <= kFusedMaxHold) return fused_by_nc<MF, 16>(p, a, lda, gpb, c, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t fused_lds_bytes(int kw, int nc, int m, int kbw) {
+  const size_t red = kw > 1 ? 2 * size_t(kw) * nc * 1024 : 0;
+  return size_t(kw) * 64 + 64 + red + size_t(kw) * m * (size_t(kbw) * 128 + 16);
+}
+
+int fused_rows(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : (m <= 8 ? 8 : 16))); }
+
+bool fused_config_supported(const SkinnyConfig& c, int m, int k) {
+  if (m < 1 || m > kFusedMaxRows || c.mr != 1) return false;
+  if (c.nc != 1 && c.nc != 2) return false;
+  if (c.kw < 1 || c.kw > 8 || !(c.kbw == 4 || c.kbw == 8 || c.kbw == 16)) return false;
+  if (c.kw * c.kbw * 128 < k) return false;
+  if (fused_rows(m) * c.kbw > kFusedMaxHold) return false;
+  if (c.wgs < 0) return false;
+  return fused_lds_bytes(c.kw, c.nc, m, c.kbw) <= kFusedMaxLds;
+}
+
+hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, int gpb,
+                             const SkinnyConfig& c, hipStream_t stream) {
+  if (!fused_config_supported(c, p.m, p.k)) return hipErrorInvalidValue;
+  switch (fused_rows(p.m)) {
+    case 1: return fused_by_kbw<1>(p, a, lda, gpb, c, stream);
+    case 2: return fused_by_kbw<2>(p, a, lda, gpb, c, stream);
+    case 4: return fused_by_kbw<4>(p, a, lda, gpb, c, stream);
+    case 8: return fused_by_kbw<8>(p, a, lda, gpb, c, stream);
+    case 16: return fused_by_kbw<16>(p, a, lda, gpb, c, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4a8

@@ -57,6 +57,7 @@ struct SkinnyConfig {
   int nc;    // 16-column tiles per wave (1 or 2)
   int kw;    // waves splitting K inside one workgroup (1..8)
   int kbw;   // 128-k blocks per wave
+  int wgs = 0;   // fused kernel: workgroups of the persistent grid (0: one per column-tile group)
 };
 
 struct TiledConfig {
@@ -85,14 +86,24 @@ bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb);
 hipError_t launch_w4a16_skinny(const Gemm16Params& p, int gpb, const SkinnyConfig& c,
                                hipStream_t stream);
 
-// Fused quantization + skinny GEMM: M <= kFusedMaxRows, one row tile, each
-// wave's K range at most 16 blocks, LDS within kFusedMaxLds.  The automatic
-// choice takes it up to kFusedAutoRows tokens: beyond that the per-workgroup
-// quantization costs more than the launch it saves (timed on MI355X over the
-// Llama-3-8B decode layers: M = 1 gains 1.6-3 us per layer, M = 4 loses).
-constexpr int kFusedMaxRows = 8;
-constexpr int kFusedAutoRows = 2;
-constexpr size_t kFusedMaxLds = 96 * 1024;
+// Fused quantization + skinny GEMM (fused.hip): M <= kFusedMaxRows, one
+// row tile, 1 or 2 column tiles per group, 4, 8 or 16 k-blocks per wave with
+// rows x blocks per wave <= kFusedMaxHold (the fp16 chunks each lane holds
+// while the row maxima are reduced: kFusedMaxHold VGPRs), LDS within
+// kFusedMaxLds.
+constexpr int kFusedMaxRows = 16;
+// Automatic choice (graph-replay timings on MI355X over the Llama-3-8B
+// decode layers): every workgroup quantizes all M x K activations, about
+// five vector instructions per element, which costs more than the launch it
+// saves from 32768 elements on (M = 8 at K = 4096, M = 4 at K = 14336);
+// below that the fused layer is 0.4-2 us faster.  The persistent grid holds
+// one workgroup per compute unit (256 on MI355X): wide layers (gate+up,
+// 896 column-tile groups) then quantize A 256 times instead of 896.
+constexpr long kFusedAutoElems = 32768;
+constexpr int kFusedAutoWgs = 256;
+constexpr int kFusedMaxHold = 64;
+constexpr size_t kFusedMaxLds = 128 * 1024;
+size_t fused_lds_bytes(int kw, int nc, int m, int kbw);
 bool fused_config_supported(const SkinnyConfig& c, int m, int k);
 hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, int gpb,
                              const SkinnyConfig& c, hipStream_t stream);

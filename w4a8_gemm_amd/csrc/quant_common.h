@@ -53,19 +53,36 @@ __device__ __forceinline__ float act_recip(uint16_t scale_bits) {
   return scale != 0.0f ? 1.0f / scale : 0.0f;
 }
 
-__device__ __forceinline__ int quant1(uint16_t h, float r) {
-  float v = __builtin_rintf(h2f(h) * r);
-  v = fminf(fmaxf(v, -127.0f), 127.0f);
-  return static_cast<int>(v);
+// int8 code of one half h under the multiplier r, as the low byte of the
+// returned word: v = fp32(h * r) is clamped to +-127 (a median of three;
+// clamping before rounding gives the same integer because the bounds are
+// integers), then rounded half to even by adding 1.5 * 2^23.  The addition
+// rounds its exact sum once, and fp32 values in [2^23, 2^24) are spaced 1
+// apart, so the sum is 1.5 * 2^23 + rint(v) exactly and its low byte is
+// rint(v) in two's complement.  The product is written as fma(h, r, +0):
+// one rounding of the exact product, as a multiply, and the hardware folds
+// the fp16 conversion into it (v_fma_mix_f32); a -0 product becomes +0,
+// which gives the same code.  The rounding add stays a separate instruction
+// (the library is built without contraction).
+__device__ __forceinline__ uint32_t quant_byte(uint16_t h, float r) {
+  const float v = __builtin_amdgcn_fmed3f(__builtin_fmaf(h2f(h), r, 0.0f), -127.0f, 127.0f);
+  return __builtin_bit_cast(uint32_t, v + 12582912.0f);
 }
 
-// four halves (two dwords) to four int8 in one dword
+__device__ __forceinline__ int quant1(uint16_t h, float r) {
+  return int(int8_t(uint8_t(quant_byte(h, r) & 0xFFu)));
+}
+
+// four halves (two dwords) to four int8 in one dword: two byte permutes
+// gather the low bytes of the four codes, a third merges the pairs
 __device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float r) {
-  uint32_t b0 = uint32_t(quant1(uint16_t(h01 & 0xFFFFu), r)) & 0xFFu;
-  uint32_t b1 = uint32_t(quant1(uint16_t(h01 >> 16), r)) & 0xFFu;
-  uint32_t b2 = uint32_t(quant1(uint16_t(h23 & 0xFFFFu), r)) & 0xFFu;
-  uint32_t b3 = uint32_t(quant1(uint16_t(h23 >> 16), r)) & 0xFFu;
-  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  const uint32_t b0 = quant_byte(uint16_t(h01 & 0xFFFFu), r);
+  const uint32_t b1 = quant_byte(uint16_t(h01 >> 16), r);
+  const uint32_t b2 = quant_byte(uint16_t(h23 & 0xFFFFu), r);
+  const uint32_t b3 = quant_byte(uint16_t(h23 >> 16), r);
+  const uint32_t p01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);   // b0.0, b1.0, 0, 0
+  const uint32_t p23 = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);   // 0, 0, b2.0, b3.0
+  return __builtin_amdgcn_perm(p23, p01, 0x07060100u);
 }
 
 // eight halves to eight int8

@@ -218,264 +218,6 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
   }
 }
 
-// ---------------------------------------------------------------- fused
-// Small M with the per-token quantization of the activations fused in
-// (one launch instead of quantizer + GEMM).  Same workgroup shape and weight
-// ring as skinny_kernel with one row tile (MR = 1), M <= MF rows.  Before
-// its K loop each wave loads its own K range of every row (fp16) into
-// registers: the waves' partial row maxima meet in LDS, every wave derives
-// s_a and 1 / s_a from them exactly as the standalone quantizer does, and
-// each wave writes its int8 slab to LDS, from where the K loop reads the
-// MFMA A operands.  The weight ring is issued before any of this, so the
-// weight stream starts at once.  Workgroup 0 also stores A8 and s_a.
-//
-// LDS: [kw][16][64] int32 split-K partials (kw > 1), then [16] s_a as
-// float, [kw][MF] uint32 row maxima, [kw][MF][slab] int8 slabs with
-// slab = kbw * 128 + 16 bytes (the 16-byte pad staggers rows over banks).
-template <int NC, int GPB, int D, int MF>
-__global__ __launch_bounds__(512) void skinny_fused_kernel(GemmParams p, const uint16_t* a,
-                                                           int lda) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int CPL = 4;            // 16-byte chunks per lane and row: kbw <= 16
-  const int lane = threadIdx.x & 63;
-  const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kw = blockDim.x >> 6;
-  const int quarter = lane >> 4;
-  const int r16 = lane & 15;
-
-  const int ntiles = p.n >> 4;
-  const int kblocks = p.k >> 7;
-  const int tile0 = blockIdx.x * NC;
-  const int kb_begin = min(kblocks, wk * p.kb_per_wave);
-  const int kb_end = min(kblocks, kb_begin + p.kb_per_wave);
-  // loads past the range re-read this block (always a valid block, also for
-  // a wave without blocks, so that the ring is issued unconditionally)
-  const int kb_last = min(kblocks - 1, max(kb_begin, kb_end - 1));
-  const int slab = p.kb_per_wave * 128 + 16;
-
-  int32_t* red = reinterpret_cast<int32_t*>(lds);
-  const int red_bytes = kw > 1 ? kw * NC * 1024 : 0;
-  float* sa_lds = reinterpret_cast<float*>(lds + red_bytes);
-  uint32_t* amax_lds = reinterpret_cast<uint32_t*>(lds + red_bytes + 64);
-  int8_t* slabs = reinterpret_cast<int8_t*>(lds + red_bytes + 64 + ((kw * MF * 4 + 15) & ~15));
-  int8_t* my_slab = slabs + wk * MF * slab;
-
-  const uint8_t* qptr[NC];
-  const uint32_t* mrow[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = min(tile0 + c, ntiles - 1);
-    qptr[c] = p.q + (size_t(t) * kblocks * 64 + lane) * 16;
-    mrow[c] = reinterpret_cast<const uint32_t*>(p.meta + size_t(t * 16 + r16) * p.meta_row_bytes);
-  }
-
-  constexpr int MSTEP = GPB == 0 ? D : 4 / GPB;
-  u32x4 q[D][NC];
-  uint32_t md[D][NC], mdn[D][NC];
-  auto issue = [&](int j, int slot_kb) {
-    const int kb = min(slot_kb, kb_last);
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      q[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qptr[c] + size_t(kb) * 1024));
-    if (j % MSTEP == 0) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) mdn[j][c] = mrow[c][GPB == 0 ? 0 : (kb * GPB) >> 2];
-    }
-  };
-  auto next_group_meta = [&]() {
-#pragma unroll
-    for (int j = 0; j < D; j += MSTEP)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) md[j][c] = mdn[j][c];
-  };
-  const bool has_work = kb_begin < kb_end;
-
-  // ---- quantization prologue: this wave's K range of rows 0 .. M-1.  The
-  // activation loads go out first and the weight ring right behind them, so
-  // that waiting for the activations (vector-memory counters complete in
-  // order) does not wait for the weights.
-  const int k0 = kb_begin * 128;
-  const int cpr = (kb_end - kb_begin) * 16;        // 16-byte chunks per row in the range
-  uint4 chunk[MF][CPL];
-  uint32_t mx[MF];
-#pragma unroll
-  for (int r = 0; r < MF; ++r) {
-    mx[r] = 0;
-    const uint16_t* src = a + size_t(min(r, p.m - 1)) * lda + k0;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = j * 64 + lane;
-      chunk[r][j] = (r < p.m && c < cpr) ? *reinterpret_cast<const uint4*>(src + c * 8)
-                                         : uint4{0, 0, 0, 0};
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < D; ++j) issue(j, kb_begin + j);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int r = 0; r < MF; ++r) {
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) mx[r] = absmax8(mx[r], chunk[r][j]);
-    uint32_t m16 = absmax_bits(mx[r]);
-    for (int off = 32; off > 0; off >>= 1) m16 = max(m16, uint32_t(__shfl_xor(int(m16), off)));
-    if (lane == 0) amax_lds[wk * MF + r] = m16;
-  }
-  __syncthreads();
-  const bool store_a8 = blockIdx.x == 0;
-#pragma unroll
-  for (int r = 0; r < MF; ++r) {
-    uint32_t am = 0;
-    for (int w = 0; w < kw; ++w) am = max(am, amax_lds[w * MF + r]);
-    const uint16_t sb = act_scale_bits(am);
-    const float rc = act_recip(sb);
-    if (wk == 0 && lane == 0 && r < p.m) {
-      sa_lds[r] = h2f(sb);
-      if (store_a8) p.s_a_out[r] = sb;
-    }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = j * 64 + lane;
-      if (r < p.m && c < cpr) {
-        const uint2 o = quant8(chunk[r][j], rc);
-        *reinterpret_cast<uint2*>(my_slab + r * slab + c * 8) = o;
-        if (store_a8) *reinterpret_cast<uint2*>(p.a8_out + size_t(r) * p.lda8 + k0 + c * 8) = o;
-      }
-    }
-  }
-  __syncthreads();   // slabs and s_a visible (each wave reads only its own slab)
-
-  float sa[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) sa[r] = sa_lds[min(4 * quarter + r, p.m - 1)];
-  float s1[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) s1[c] = h2f(p.s1[min((tile0 + c) * 16 + r16, p.n - 1)]);
-
-  // A operand of lane (row r16, k-quarter) for block kb, half h, from the
-  // slab; rows past M read row M - 1 (never stored)
-  const int8_t* arow = my_slab + min(r16, p.m - 1) * slab + 16 * quarter;
-  v4i acc[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = v4i{0, 0, 0, 0};
-
-  auto compute = [&](int j, int kb) {
-    const u32x4 (&qs)[NC] = q[j];
-    const uint32_t (&ms)[NC] = md[j - j % MSTEP];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const v4i af = *reinterpret_cast<const v4i*>(arow + (kb - kb_begin) * 128 + 64 * h);
-      int byte = 0;
-      if (GPB == 1) byte = kb & 3;
-      if (GPB == 2) byte = 2 * (kb & 1) + h;
-      if (GPB == 4) byte = 2 * h + (quarter >> 1);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const GroupConst gc = group_const((ms[c] >> (8 * byte)) & 0xFFu);
-        const uint32_t w0 = h ? qs[c].z : qs[c].x;
-        const uint32_t w1 = h ? qs[c].w : qs[c].y;
-        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, decode16(w0, w1, gc), acc[c], 0, 0, 0);
-      }
-    }
-  };
-
-  if (has_work) {
-    next_group_meta();
-    int kb0 = kb_begin;
-    for (; kb0 + D < kb_end; kb0 += D) {
-#pragma unroll
-      for (int j = 0; j < D; ++j) {
-        compute(j, kb0 + j);
-        issue(j, kb0 + D + j);
-      }
-      next_group_meta();
-    }
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (kb0 + j < kb_end) compute(j, kb0 + j);
-  }
-
-  if (kw == 1) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (tile0 + c >= ntiles) continue;
-      int32_t v[4] = {acc[c][0], acc[c][1], acc[c][2], acc[c][3]};
-      store_frag(p, 0, (tile0 + c) * 16, lane, v, s1[c], sa);
-    }
-    return;
-  }
-  int32_t* mine = red + wk * NC * 256;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mine[(c * 4 + r) * 64 + lane] = acc[c][r];
-  __syncthreads();
-  for (int c = wk; c < NC; c += kw) {
-    if (tile0 + c >= ntiles) continue;
-    int32_t v[4] = {0, 0, 0, 0};
-    for (int w = 0; w < kw; ++w) {
-      const int32_t* part = red + (w * NC + c) * 256;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += part[r * 64 + lane];
-    }
-    float s1c = s1[0];
-#pragma unroll
-    for (int cc = 1; cc < NC; ++cc)
-      if (cc == c) s1c = s1[cc];
-    store_frag(p, 0, (tile0 + c) * 16, lane, v, s1c, sa);
-  }
-}
-
-size_t fused_lds_bytes(int kw, int nc, int mf, int kbw) {
-  const size_t red = kw > 1 ? size_t(kw) * nc * 1024 : 0;
-  return red + 64 + ((size_t(kw) * mf * 4 + 15) & ~size_t(15)) + size_t(kw) * mf * (kbw * 128 + 16);
-}
-
-template <int NC, int GPB, int MF>
-hipError_t launch_fused_t(const GemmParams& p, const uint16_t* a, int lda, const SkinnyConfig& c,
-                          hipStream_t stream) {
-  constexpr int D = 4;
-  const void* fn = reinterpret_cast<const void*>(&skinny_fused_kernel<NC, GPB, D, MF>);
-  const size_t lds = fused_lds_bytes(c.kw, NC, MF, c.kbw);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-  }
-  const int ntiles = p.n / 16;
-  GemmParams arg = p;
-  arg.kb_per_wave = c.kbw;
-  const uint16_t* a_arg = a;
-  int lda_arg = lda;
-  void* args[] = {&arg, &a_arg, &lda_arg};
-  return hipLaunchKernel(fn, dim3((ntiles + NC - 1) / NC), dim3(64 * c.kw), args, lds, stream);
-}
-
-template <int NC, int MF>
-hipError_t fused_by_gpb(const GemmParams& p, const uint16_t* a, int lda, int gpb,
-                        const SkinnyConfig& c, hipStream_t s) {
-  switch (gpb) {
-    case 0: return launch_fused_t<NC, 0, MF>(p, a, lda, c, s);
-    case 1: return launch_fused_t<NC, 1, MF>(p, a, lda, c, s);
-    case 2: return launch_fused_t<NC, 2, MF>(p, a, lda, c, s);
-    case 4: return launch_fused_t<NC, 4, MF>(p, a, lda, c, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int MF>
-hipError_t fused_by_nc(const GemmParams& p, const uint16_t* a, int lda, int gpb,
-                       const SkinnyConfig& c, hipStream_t s) {
-  switch (c.nc) {
-    case 1: return fused_by_gpb<1, MF>(p, a, lda, gpb, c, s);
-    case 2: return fused_by_gpb<2, MF>(p, a, lda, gpb, c, s);
-    case 4:
-      // four column tiles only up to 4 rows (register budget)
-      if constexpr (MF <= 4) return fused_by_gpb<4, MF>(p, a, lda, gpb, c, s);
-      return hipErrorInvalidValue;
-  }
-  return hipErrorInvalidValue;
-}
-
 template <int MR, int NC, int GPB>
 hipError_t launch_skinny(const GemmParams& p, const SkinnyConfig& c, hipStream_t stream) {
   constexpr int D = 4;
@@ -511,28 +253,6 @@ bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb) {
   (void)gpb;
   if (c.kw < 1 || c.kw > 8 || c.kbw < 1 || c.kbw % 4) return false;   // ring groups of 4
   return c.kw * c.kbw * 128 >= k;                    // the waves cover all of K
-}
-
-int fused_rows(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : 8)); }
-
-bool fused_config_supported(const SkinnyConfig& c, int m, int k) {
-  if (m < 1 || m > kFusedMaxRows || c.mr != 1) return false;
-  if (!(c.nc == 1 || c.nc == 2 || (c.nc == 4 && m <= 4))) return false;
-  if (c.kw < 1 || c.kw > 8 || c.kbw < 4 || c.kbw > 16 || c.kbw % 4) return false;
-  if (c.kw * c.kbw * 128 < k) return false;
-  return fused_lds_bytes(c.kw, c.nc, fused_rows(m), c.kbw) <= kFusedMaxLds;
-}
-
-hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, int gpb,
-                             const SkinnyConfig& c, hipStream_t stream) {
-  if (!fused_config_supported(c, p.m, p.k)) return hipErrorInvalidValue;
-  switch (fused_rows(p.m)) {
-    case 1: return fused_by_nc<1>(p, a, lda, gpb, c, stream);
-    case 2: return fused_by_nc<2>(p, a, lda, gpb, c, stream);
-    case 4: return fused_by_nc<4>(p, a, lda, gpb, c, stream);
-    case 8: return fused_by_nc<8>(p, a, lda, gpb, c, stream);
-  }
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_skinny(const GemmParams& p, int gpb, const SkinnyConfig& c,
