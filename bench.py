@@ -351,6 +351,7 @@ def main():
     gemm_us = np.array(per_step_gemm) * 1e3
     med_us = np.median(gemm_us, axis=0)
     mean_us = gemm_us.mean(axis=0)
+    p10_us, p90_us = np.percentile(gemm_us, 10, axis=0), np.percentile(gemm_us, 90, axis=0)
     step_bytes = sum(w4a16_bytes(m, n, k, g) if args.w4a16 else
                      algo_bytes(m, n, k, g) + quant_bytes(m, k) for (m, _, n, k, g, _) in runs)
     step_ops = sum(2.0 * m * n * k for (m, _, n, k, g, _) in runs)
@@ -366,6 +367,8 @@ def main():
         table.append({"m": m, "layer": layer, "n": n, "k": k, "g": g, "fused": fused[r],
                       "gemm_us_median": round(float(med_us[r]), 3),
                       "gemm_us_mean": round(float(mean_us[r]), 3),
+                      "gemm_us_p10": round(float(p10_us[r]), 3),
+                      "gemm_us_p90": round(float(p90_us[r]), 3),
                       "GBps": round(gemm_bytes[r] / t / 1e9, 1),
                       "TOPS": round(gemm_ops[r] / t / 1e12, 2),
                       "frac_hbm": round(gemm_bytes[r] / t / 1e9 / HBM_PEAK_GBS, 3),

@@ -169,11 +169,14 @@ typedef struct {
                     w4a8_linear only: 3 fused quantization + skinny */
   int k_split;   /* skinny: waves that split K inside a workgroup (1..8);
                     tiled: wave groups that split the k-blocks inside a
-                    workgroup (1, or 2 with m_tiles 4 or 8, 2 stages);
+                    workgroup (1, or 2: m_tiles x n_tiles 8 x 4 or 4 x 4
+                    with 2 stages, 8 x 2 with 2-3, 4 x 2 with 2-4);
                     0 = auto */
   int n_tiles;   /* 16-column tiles per wave: skinny 1, 2 or 4; tiled 2 or 4; 0 = auto */
   int m_tiles;   /* tiled: 16-row tiles per wave (4 or 8), 0 = auto */
-  int stages;    /* tiled: LDS pipeline stages (2 or 3), 0 = auto */
+  int stages;    /* tiled: LDS pipeline stages, 0 = auto; four-wave tiles
+                    (m_tiles x n_tiles) 8 x 4: 2-4, 4 x 4: 2-5, 8 x 2: 2-6,
+                    4 x 2: 2, 3, 4, 6 or 8; eight-wave tiles as below */
   int row_groups;/* tiled: waves along M per workgroup: 1 (4 waves) or 2
                     (8 waves, 256 x 256 tiles, m_tiles 8 and 3 stages only),
                     0 = auto */

@@ -234,11 +234,14 @@ def test_gpu_entry_points_validate_before_any_hip_call():
     assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 2   # skinny is M <= 64
     # tiled shapes that do not exist: 8-wave tiles only as 8 x 4 tiles per
     # wave with 3 stages (row groups) or 2 stages (k-groups), never both;
-    # row groups and k-groups 1 or 2; stages 2 or 3
+    # row groups and k-groups 1 or 2; four-wave tiles only to the pipeline
+    # depth that fits LDS (8 x 4: 4, 4 x 4: 5, 8 x 2: 6, 4 x 2: 8, not 5 or 7)
     for v, ks, nt, mt, st, rg in ((2, 0, 0, 4, 0, 2), (2, 0, 0, 8, 2, 2), (2, 0, 2, 8, 3, 2),
-                                  (2, 0, 0, 0, 0, 3), (2, 0, 0, 8, 4, 1), (2, 0, 0, 6, 0, 1),
-                                  (2, 3, 0, 0, 0, 0), (2, 2, 2, 8, 0, 0), (2, 2, 0, 8, 3, 0),
-                                  (2, 2, 0, 8, 0, 2)):
+                                  (2, 0, 0, 0, 0, 3), (2, 0, 0, 8, 5, 1), (2, 0, 0, 6, 0, 1),
+                                  (2, 0, 4, 4, 6, 1), (2, 0, 2, 8, 7, 1), (2, 0, 2, 4, 5, 1),
+                                  (2, 0, 2, 4, 9, 1), (2, 0, 2, 4, 1, 1),
+                                  (2, 3, 0, 0, 0, 0), (2, 2, 2, 8, 4, 0), (2, 2, 0, 8, 3, 0),
+                                  (2, 2, 2, 4, 5, 0), (2, 2, 0, 8, 0, 2)):
         opts = w4.GemmOpts(v, ks, nt, mt, st, rg)
         assert call(m=100, lda8=512, opts=ctypes.byref(opts)) == 1, (mt, st, rg)
     # K split over workgroups: at most 16 slices; the workspace must hold

@@ -205,7 +205,15 @@ def test_gemm_tiled_every_tile_shape(m, n, k, g):
     blob = w4.pack(w, g)
     for mt, nt, rg, st, ks in ((0, 0, 0, 0, 0), (4, 4, 1, 2, 0), (4, 4, 1, 3, 0), (8, 4, 1, 2, 0),
                                (8, 4, 1, 3, 0), (8, 2, 1, 3, 0), (8, 4, 2, 0, 0), (8, 4, 1, 0, 2),
-                               (4, 4, 1, 0, 2)):
+                               (4, 4, 1, 0, 2),
+                               # deeper pipelines (more stages than k-blocks at k = 256) and
+                               # 64 x 128 tiles
+                               (8, 4, 1, 4, 0), (4, 4, 1, 4, 0), (4, 4, 1, 5, 0), (8, 2, 1, 2, 0),
+                               (8, 2, 1, 4, 0), (8, 2, 1, 5, 0), (8, 2, 1, 6, 0), (4, 2, 1, 2, 0),
+                               (4, 2, 1, 3, 0), (4, 2, 1, 4, 0), (4, 2, 1, 6, 0), (4, 2, 1, 8, 0),
+                               # two k-groups on 128-column tiles
+                               (8, 2, 1, 2, 2), (8, 2, 1, 3, 2), (4, 2, 1, 2, 2), (4, 2, 1, 3, 2),
+                               (4, 2, 1, 4, 2)):
         log(f"gemm tiled m={m} n={n} k={k} g={g} m_tiles={mt} n_tiles={nt} row_groups={rg} "
             f"stages={st} k_split={ks}")
         y, acc = run_gemm(out["a8"], out["s_a"], blob, n, k, g, variant=2, m_tiles=mt,
@@ -226,13 +234,16 @@ def test_gemm_tiled_k_slices_exact(m, n, k, g):
     s_a = torch.from_numpy(out["s_a"]).to(dev)
     wdev = w4.to_device(blob, dev)
     kblocks = k // 128
-    for sl, mt, ks in ((2, 8, 0), (3, 4, 0), (5, 8, 2), (min(kblocks, 16), 4, 2), (16, 8, 0)):
+    for sl, mt, nt, st, ks in ((2, 8, 0, 0, 0), (3, 4, 0, 0, 0), (5, 8, 0, 0, 2),
+                               (min(kblocks, 16), 4, 0, 0, 2), (16, 8, 0, 0, 0),
+                               (2, 8, 2, 6, 0), (3, 4, 2, 8, 0), (4, 4, 4, 5, 0), (3, 4, 2, 4, 2)):
         ws = torch.full((16 * m * n * 4 + 64,), 0x5A, dtype=torch.uint8, device=dev)
-        log(f"gemm tiled slices={sl} m={m} n={n} k={k} g={g} m_tiles={mt} k_split={ks}")
+        log(f"gemm tiled slices={sl} m={m} n={n} k={k} g={g} m_tiles={mt} n_tiles={nt} "
+            f"stages={st} k_split={ks}")
         y, acc = w4.gemm(a8, s_a, wdev, n, k, g, want_acc=True, variant=2, m_tiles=mt,
-                         k_split=ks, slices=sl, workspace=ws)
+                         n_tiles=nt, stages=st, k_split=ks, slices=sl, workspace=ws)
         torch.cuda.synchronize()
-        assert np.array_equal(acc.cpu().numpy(), out["acc"]), (sl, mt, ks)
+        assert np.array_equal(acc.cpu().numpy(), out["acc"]), (sl, mt, nt, st, ks)
         assert ref.y_tolerance_ok(y.cpu().numpy(), out["y"]).all()
 
 

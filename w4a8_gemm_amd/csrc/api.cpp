@@ -115,16 +115,19 @@ struct Plan {
   size_t workspace = 0;     // bytes
 };
 
-// Tiles of the four-wave and eight-wave tiled kernels.
-long tiled_tiles(int m, int n, int rows) {
-  return long((m + rows - 1) / rows) * long((n / kColTile + 15) / 16);
+// Workgroup tiles of rows x cols over the output.
+long tiled_tiles(int m, int n, int rows, int cols = 256) {
+  return long((m + rows - 1) / rows) * long((n + cols - 1) / cols);
 }
 
 Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   Plan pl;
   pl.variant = opts ? opts->variant : 0;
   if (pl.variant < 0 || pl.variant > 2) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
-  if (pl.variant == 0) pl.variant = m <= 64 ? 1 : 2;
+  // the skinny kernel up to 16 tokens, and up to 64 unless the layer is
+  // wide enough to give the tiled kernel's 64 x 128 tiles most of the GPU
+  // (its activation fragments, re-read by every workgroup, grow with M)
+  if (pl.variant == 0) pl.variant = (m <= 16 || (m <= 64 && tiled_tiles(m, n, 64, 128) < 192)) ? 1 : 2;
   const int kblocks = k / kKBlock;
   if (pl.variant == 1) {
     if (m > 64) { pl.status = W4A8_ERR_UNSUPPORTED; return pl; }
@@ -137,41 +140,50 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     }
     return pl;
   }
-  // Tiled (choices from timing sweeps on the layer shapes): 256 x 256 tiles
-  // of eight waves with 3 stages when they fill every compute unit at least
-  // once; else 128 x 256 tiles of four waves with 2 stages (two workgroups
-  // per compute unit) when there are enough of them; else, for at most 64
-  // such tiles or K of at least 8192, the same tiles with K split over 2..8
-  // workgroups so that about 384 workgroups run (each slice keeps at least
-  // 4 k-blocks); else 64 x 256 tiles with 3 stages.
+  // Tiled (choices from graph-replay timing sweeps on the Llama-3-8B layer
+  // shapes, M = 32 .. 1024): the kernel needs about one workgroup of eight
+  // waves, or two of four, per compute unit, so the tile shrinks with the
+  // grid it yields:
+  //   >= 224 tiles of 256 x 256          -> 256 x 256, eight waves, 3 stages
+  //   K >= 8192 and < 192 of 128 x 256   -> 128 x 256 with K split over
+  //                                         2..8 workgroups (~384 in all)
+  //   >= 256 tiles of 128 x 128, M > 64 -> 128 x 128, four waves, 3 stages
+  //   >= 192 tiles of 128 x 128, M > 64 -> 128 x 128, two k-groups, 2 stages
+  //   otherwise                          -> 64 x 128, two k-groups, 3 stages
+  // (at M <= 64 a 128-row tile is half empty: 64 x 128 tiles, same count)
+  // Forced options select among the four-wave kernels (or the eight-wave
+  // ones they name) with the rest from the 128 x 256 defaults.
   TiledConfig& c = pl.tiled;
   c.nw = 4;
-  c.nc = 4;
-  const long tiles256 = tiled_tiles(m, n, 256);
-  const long tiles128 = tiled_tiles(m, n, 128);
-  c.rw = tiles256 >= 256 ? 2 : 1;
-  c.kg = 1;
-  // a forced row-tile, stage or k-group count without a forced row-group
-  // count selects among the four-wave-per-k-group kernels
-  if (opts && (opts->m_tiles > 0 || opts->stages > 0 || opts->k_split > 0)) c.rw = 1;
-  if (opts && opts->row_groups > 0) c.rw = opts->row_groups;
-  if (opts && opts->k_split > 0) c.kg = opts->k_split;
-  c.mr = (c.rw == 2 || tiles128 >= 192) ? 8 : 4;
-  if (opts && opts->m_tiles > 0) c.mr = opts->m_tiles;
-  c.stages = (c.rw == 2 || (c.mr == 4 && c.kg == 1)) ? 3 : 2;
-  if (opts && opts->stages > 0) c.stages = opts->stages;
-  if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
-  int slices = 1;
+  const long t256 = tiled_tiles(m, n, 256);
+  const long t128x256 = tiled_tiles(m, n, 128);
+  const long t128x128 = tiled_tiles(m, n, 128, 128);
   const bool forced = opts && (opts->m_tiles > 0 || opts->stages > 0 || opts->k_split > 0 ||
                                opts->row_groups > 0 || opts->n_tiles > 0 || opts->slices > 0);
-  if (!forced && c.rw == 1 && tiles128 < 192 && (tiles128 <= 64 || kblocks >= 64)) {
-    const long want = (384 + tiles128 - 1) / tiles128;
-    const int most = std::min(8, kblocks / 4);
-    if (most >= 2) {
-      slices = int(std::max(2L, std::min<long>(want, most)));
-      c.mr = 8;
-      c.stages = 2;
-    }
+  int slices = 1;
+  if (forced) {
+    c.nc = 4;
+    c.rw = 1;
+    c.kg = 1;
+    if (opts->row_groups > 0) c.rw = opts->row_groups;
+    if (opts->k_split > 0) c.kg = opts->k_split;
+    c.mr = (c.rw == 2 || t128x256 >= 192) ? 8 : 4;
+    if (opts->m_tiles > 0) c.mr = opts->m_tiles;
+    c.stages = (c.rw == 2 || (c.mr == 4 && c.kg == 1)) ? 3 : 2;
+    if (opts->stages > 0) c.stages = opts->stages;
+    if (opts->n_tiles > 0) c.nc = opts->n_tiles;
+  } else if (t256 >= 224) {
+    c = TiledConfig{8, 4, 4, 2, 1, 3};
+  } else if (kblocks >= 64 && t128x256 < 192) {
+    c = TiledConfig{8, 4, 4, 1, 1, 2};
+    const long want = (384 + t128x256 - 1) / t128x256;
+    slices = int(std::max(2L, std::min<long>(want, 8)));
+  } else if (m > 64 && t128x128 >= 256) {
+    c = TiledConfig{8, 2, 4, 1, 1, 3};
+  } else if (m > 64 && t128x128 >= 192) {
+    c = TiledConfig{8, 2, 4, 1, 2, 2};
+  } else {
+    c = TiledConfig{4, 2, 4, 1, 2, 3};
   }
   if (opts && opts->slices > 0) slices = opts->slices;
   if (slices > kMaxSlices) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }

@@ -86,6 +86,7 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int* bm, int*
 }
 
 constexpr int kColGroups = 4;   // waves along N per workgroup
+constexpr int kTiledMaxLds = 160 * 1024;   // LDS of one gfx950 compute unit
 
 // One LDS stage: for each of the KG k-groups, the activation tile, weight
 // codes and meta of one k-block.
@@ -380,15 +381,56 @@ hipError_t tiled_by_gpb(const GemmParams& p, int gpb, int sl, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Four-wave tiles (RW = KG = 1) and their pipeline depths.  Deeper
+// pipelines keep more k-blocks in flight per workgroup, which is what a
+// grid of about one workgroup per compute unit needs to cover the memory
+// latency; each depth fits the 160 KB of LDS and the vmcnt range.
+bool four_wave_stages_ok(int mr, int nc, int s) {
+  if (mr == 8 && nc == 4) return s >= 2 && s <= 4;
+  if (mr == 4 && nc == 4) return s >= 2 && s <= 5;
+  if (mr == 8 && nc == 2) return s >= 2 && s <= 6;
+  if (mr == 4 && nc == 2) return s == 2 || s == 3 || s == 4 || s == 6 || s == 8;
+  return false;
+}
+
+// Two k-groups of four waves (eight waves, KG = 2): the 256-column tiles
+// with 2 stages, the 128-column tiles deeper.
+bool two_group_stages_ok(int mr, int nc, int s) {
+  if (nc == 4) return (mr == 8 || mr == 4) && s == 2;
+  if (mr == 8 && nc == 2) return s == 2 || s == 3;
+  if (mr == 4 && nc == 2) return s >= 2 && s <= 4;
+  return false;
+}
+
+template <int MR, int NC>
+hipError_t four_wave_by_stages(const GemmParams& p, int gpb, int stages, int sl, hipStream_t s) {
+  switch (stages) {
+    case 2: return tiled_by_gpb<MR, NC, 1, 1, 2>(p, gpb, sl, s);
+    case 3: return tiled_by_gpb<MR, NC, 1, 1, 3>(p, gpb, sl, s);
+    case 4: return tiled_by_gpb<MR, NC, 1, 1, 4>(p, gpb, sl, s);
+    case 5:
+      if constexpr (5 * tiled_stage_bytes<MR, NC, 1, 1>() <= kTiledMaxLds)
+        return tiled_by_gpb<MR, NC, 1, 1, 5>(p, gpb, sl, s);
+      break;
+    case 6:
+      if constexpr (6 * tiled_stage_bytes<MR, NC, 1, 1>() <= kTiledMaxLds)
+        return tiled_by_gpb<MR, NC, 1, 1, 6>(p, gpb, sl, s);
+      break;
+    case 8:
+      if constexpr (8 * tiled_stage_bytes<MR, NC, 1, 1>() <= kTiledMaxLds)
+        return tiled_by_gpb<MR, NC, 1, 1, 8>(p, gpb, sl, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool tiled_config_supported(const TiledConfig& c) {
   if (c.nw != kColGroups) return false;
   if (c.rw == 2) return c.kg == 1 && c.mr == 8 && c.nc == 4 && c.stages == 3;
-  if (c.kg == 2) return c.rw == 1 && (c.mr == 8 || c.mr == 4) && c.nc == 4 && c.stages == 2;
-  const bool stages_ok = c.stages == 2 || c.stages == 3;
-  return c.rw == 1 && c.kg == 1 && stages_ok &&
-         ((c.mr == 8 && c.nc == 4) || (c.mr == 4 && c.nc == 4) || (c.mr == 8 && c.nc == 2));
+  if (c.kg == 2) return c.rw == 1 && two_group_stages_ok(c.mr, c.nc, c.stages);
+  return c.rw == 1 && c.kg == 1 && four_wave_stages_ok(c.mr, c.nc, c.stages);
 }
 
 hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c, int sl,
@@ -398,18 +440,23 @@ hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c,
     return hipErrorInvalidValue;
   if (c.rw == 2) return tiled_by_gpb<8, 4, 2, 1, 3>(p, gpb, sl, stream);
   if (c.kg == 2) {
-    if (c.mr == 8) return tiled_by_gpb<8, 4, 1, 2, 2>(p, gpb, sl, stream);
-    return tiled_by_gpb<4, 4, 1, 2, 2>(p, gpb, sl, stream);
+    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 2, 2>(p, gpb, sl, stream);
+    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 2, 2>(p, gpb, sl, stream);
+    if (c.mr == 8 && c.nc == 2) {
+      if (c.stages == 2) return tiled_by_gpb<8, 2, 1, 2, 2>(p, gpb, sl, stream);
+      return tiled_by_gpb<8, 2, 1, 2, 3>(p, gpb, sl, stream);
+    }
+    if (c.mr == 4 && c.nc == 2) {
+      if (c.stages == 2) return tiled_by_gpb<4, 2, 1, 2, 2>(p, gpb, sl, stream);
+      if (c.stages == 3) return tiled_by_gpb<4, 2, 1, 2, 3>(p, gpb, sl, stream);
+      return tiled_by_gpb<4, 2, 1, 2, 4>(p, gpb, sl, stream);
+    }
+    return hipErrorInvalidValue;
   }
-  if (c.stages == 3) {
-    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 1, 3>(p, gpb, sl, stream);
-    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 1, 3>(p, gpb, sl, stream);
-    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 1, 3>(p, gpb, sl, stream);
-  } else {
-    if (c.mr == 8 && c.nc == 4) return tiled_by_gpb<8, 4, 1, 1, 2>(p, gpb, sl, stream);
-    if (c.mr == 4 && c.nc == 4) return tiled_by_gpb<4, 4, 1, 1, 2>(p, gpb, sl, stream);
-    if (c.mr == 8 && c.nc == 2) return tiled_by_gpb<8, 2, 1, 1, 2>(p, gpb, sl, stream);
-  }
+  if (c.mr == 8 && c.nc == 4) return four_wave_by_stages<8, 4>(p, gpb, c.stages, sl, stream);
+  if (c.mr == 4 && c.nc == 4) return four_wave_by_stages<4, 4>(p, gpb, c.stages, sl, stream);
+  if (c.mr == 8 && c.nc == 2) return four_wave_by_stages<8, 2>(p, gpb, c.stages, sl, stream);
+  if (c.mr == 4 && c.nc == 2) return four_wave_by_stages<4, 2>(p, gpb, c.stages, sl, stream);
   return hipErrorInvalidValue;
 }
 
