@@ -135,9 +135,11 @@ class HipEvent:
         return ms.value
 
 
-def cpu_baseline(runs, weights, budget_s=15.0):
+def cpu_baseline(runs, weights, unit, budget_s=15.0):
     """The oracle, untuned, on a bounded sample of the same workload: every
-    run, restricted to the first `cols` output columns of each layer."""
+    run, restricted to the first `cols` output columns of each layer.  The
+    rate is in the metric's unit (GB/s of algorithmic bytes, or TOPS); the
+    time of each oracle stage is reported beside it."""
     from oracle import ref
     try:
         from threadpoolctl import threadpool_info
@@ -151,25 +153,37 @@ def cpu_baseline(runs, weights, budget_s=15.0):
     acts = {}
     for (m, layer, n, k, g, seed) in runs:
         acts[(m, layer)] = synth.activations(m, k, seed=seed)
-    done_bytes = 0.0
+    done_bytes = done_ops = 0.0
+    stage = {"quant_act": 0.0, "decode_and_gemm": 0.0, "epilogue": 0.0}
     t0 = time.perf_counter()
     passes = 0
     while True:
         for (m, layer, n, k, g, seed) in runs:
             a = acts[(m, layer)]
+            t1 = time.perf_counter()
             a8, s_a = ref.quant_act(a)
+            t2 = time.perf_counter()
             w8hat = ref.decoded_weights(qws[layer])
             acc = ref.gemm_acc(a8, w8hat)
+            t3 = time.perf_counter()
             ref.epilogue(acc, s_a, qws[layer]["s1"])
-            done_bytes += algo_bytes(m, cols, k, g) + quant_bytes(m, k)
+            t4 = time.perf_counter()
+            stage["quant_act"] += t2 - t1
+            stage["decode_and_gemm"] += t3 - t2
+            stage["epilogue"] += t4 - t3
+            ncols = min(cols, n)
+            done_bytes += algo_bytes(m, ncols, k, g) + quant_bytes(m, k)
+            done_ops += 2.0 * m * ncols * k
         passes += 1
         if time.perf_counter() - t0 >= budget_s or passes >= 200:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+    value = done_ops / dt / 1e12 if unit == "TOPS" else done_bytes / dt / 1e9
+    return {"value": round(value, 4), "unit": unit, "cores": int(cores),
             "kind": "oracle",
             "sample": f"every run of the workload restricted to the first {cols} output "
-                      f"columns of each layer, {passes} pass(es), {dt:.1f} s"}
+                      f"columns of each layer, {passes} pass(es), {dt:.1f} s",
+            "stage_seconds": {key: round(v, 3) for key, v in stage.items()}}
 
 
 def main():
@@ -437,7 +451,7 @@ def main():
     if not args.no_cpu_baseline:
         sample_runs = [r for r in runs]
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(sample_runs, weights)
+        result["cpu_baseline"] = cpu_baseline(sample_runs, weights, metric_unit)
     print(json.dumps(result), flush=True)
 
 
