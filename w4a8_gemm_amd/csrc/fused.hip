@@ -16,11 +16,12 @@
 // Prologue: each wave loads its K range of rows 0 .. M-1 (fp16, 16-byte
 // chunks spread over all 64 lanes) into registers; the weight ring of the
 // first tile group is issued right behind those loads, so the weight stream
-// starts at once.  The waves' partial row maxima meet in LDS; every wave
-// derives s_a and fp32(1 / s_a) as the standalone quantizer does (the same
-// device functions, so the same bits) and writes its int8 rows to its LDS
-// slab, from which the K loop reads the MFMA A operands.  Workgroup 0 also
-// stores A8 and s_a.
+// starts at once.  The waves' partial row maxima meet in LDS (a transposed
+// shuffle reduction leaves each lane with one row); every lane derives the
+// s_a and fp32(1 / s_a) of one row as the standalone quantizer does (the same
+// device functions, so the same bits), so all rows take their divisions at
+// once, and each wave writes its int8 rows to its LDS slab, from which the K
+// loop reads the MFMA A operands.  Workgroup 0 also stores A8 and s_a.
 //
 // Weight ring: slot j = v % D holds block v of the wave's range; once block
 // v has been multiplied the slot is refilled with block v + D, which past the
@@ -124,33 +125,56 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
 #pragma unroll
   for (int j = 0; j < D; ++j) issue(j, tg0, j);
   __builtin_amdgcn_sched_barrier(0);
+  // Row maxima, all rows at once: each lane starts with its partial maximum
+  // of every row; a transposed butterfly halves the rows a lane holds at each
+  // of the first log2(MF) exchange steps (the lanes with the offset bit set
+  // keep the upper half), so afterwards lane l holds row l / (64 / MF), and
+  // the remaining steps reduce over the lanes that share a row.
+  uint32_t pm[MF];
 #pragma unroll
   for (int r = 0; r < MF; ++r) {
     uint32_t mx = 0;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) mx = absmax8(mx, chunk[r][j]);
-    uint32_t m16 = absmax_bits(mx);
-    for (int off = 32; off > 0; off >>= 1) m16 = max(m16, uint32_t(__shfl_xor(int(m16), off)));
-    if (lane == 0) amax_lds[wk * 16 + r] = m16;
+    pm[r] = absmax_bits(mx);
   }
+#pragma unroll
+  for (int off = 32, nr = MF; off > 0; off >>= 1) {
+    if (nr > 1) {
+      const bool upper = (lane & off) != 0;
+#pragma unroll
+      for (int i = 0; i < nr / 2; ++i) {
+        const uint32_t send = upper ? pm[i] : pm[i + nr / 2];
+        const uint32_t keep = upper ? pm[i + nr / 2] : pm[i];
+        pm[i] = max(keep, uint32_t(__shfl_xor(int(send), off)));
+      }
+      nr /= 2;
+    } else {
+      pm[0] = max(pm[0], uint32_t(__shfl_xor(int(pm[0]), off)));
+    }
+  }
+  constexpr int LPR = 64 / MF;   // lanes per row after the butterfly
+  if (lane % LPR == 0) amax_lds[wk * 16 + lane / LPR] = pm[0];
   __syncthreads();
+  // lane l derives the scale of row l % 16 (rows past M have maximum 0)
   const bool store_a8 = blockIdx.x == 0;
+  uint32_t am = 0;
+  for (int w = 0; w < kw; ++w) am = max(am, r16 < MF ? amax_lds[w * 16 + r16] : 0u);
+  const uint16_t sb = act_scale_bits(am);
+  const float rc = act_recip(sb);
+  if (wk == 0 && quarter == 0 && r16 < p.m) {
+    sa_lds[r16] = h2f(sb);
+    if (store_a8) p.s_a_out[r16] = sb;
+  }
 #pragma unroll
   for (int r = 0; r < MF; ++r) {
     if (r >= p.m) continue;   // (not break: the loop must stay unrolled)
-    uint32_t am = 0;
-    for (int w = 0; w < kw; ++w) am = max(am, amax_lds[w * 16 + r]);
-    const uint16_t sb = act_scale_bits(am);
-    const float rc = act_recip(sb);
-    if (wk == 0 && lane == 0) {
-      sa_lds[r] = h2f(sb);
-      if (store_a8) p.s_a_out[r] = sb;
-    }
+    const float rcr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rc), r));
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = j * 64 + lane;
       if (c < cpr) {
-        const uint2 o = quant8(chunk[r][j], rc);
+        const uint2 o = quant8(chunk[r][j], rcr);
         *reinterpret_cast<uint2*>(my_slab + r * slab + c * 8) = o;
         if (store_a8) *reinterpret_cast<uint2*>(p.a8_out + size_t(r) * p.lda8 + k0 + c * 8) = o;
       }
