@@ -315,7 +315,7 @@ def test_linear_validates_before_any_hip_call():
 
 
 def test_linear_launch_plan():
-    """w4a8_linear_launches: one fused launch below 32768 activations
+    """w4a8_linear_launches: one fused launch up to 32768 activations
     (M x K) where the fused kernel applies, two otherwise, three when the
     GEMM splits K over workgroups; forced, the fused kernel takes up to 16
     tokens (rows x k-blocks per wave within its budget, wave ranges of at
@@ -327,7 +327,8 @@ def test_linear_launch_plan():
     assert L.w4a8_linear_launches(4, 4096, 4096, 128, None) == 1
     assert L.w4a8_linear_launches(2, 4096, 14336, 128, None) == 1
     assert L.w4a8_linear_launches(2, 256, 1024, 1, None) == 1         # codebook weights
-    assert L.w4a8_linear_launches(8, 4096, 4096, 128, None) == 2      # 32768 activations
+    assert L.w4a8_linear_launches(8, 4096, 4096, 128, None) == 1      # 32768 activations
+    assert L.w4a8_linear_launches(9, 4096, 4096, 128, None) == 2
     assert L.w4a8_linear_launches(4, 4096, 14336, 128, None) == 2
     assert L.w4a8_linear_launches(16, 4096, 4096, 128, None) == 2
     assert L.w4a8_linear_launches(17, 4096, 4096, 128, None) == 2

@@ -286,9 +286,9 @@ SkinnyConfig fused_plan(int m, int n, int k, const w4a8_gemm_opts* opts) {
   return c;
 }
 
-// The automatic choice runs the fused kernel wherever it applies for fewer
-// than kFusedAutoElems activations.
-bool fused_by_default(int m, int k) { return long(m) * k < kFusedAutoElems; }
+// The automatic choice runs the fused kernel wherever it applies for up to
+// kFusedAutoElems activations.
+bool fused_by_default(int m, int k) { return long(m) * k <= kFusedAutoElems; }
 
 }  // namespace
 

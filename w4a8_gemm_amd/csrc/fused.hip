@@ -138,17 +138,24 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
     for (int j = 0; j < CPL; ++j) mx = absmax8(mx, chunk[r][j]);
     pm[r] = absmax_bits(mx);
   }
+  // (the step count and row counts are closed forms of the unrolled step
+  // index, so every pm index is a compile-time constant)
 #pragma unroll
-  for (int off = 32, nr = MF; off > 0; off >>= 1) {
-    if (nr > 1) {
-      const bool upper = (lane & off) != 0;
+  for (int step = 0; step < 6; ++step) {
+    const int off = 32 >> step;
+    const int half = (MF >> step) / 2;   // rows handed over at this step (0: none)
+    if (half > 0) {
+      // lanes with the offset bit set keep the upper half: a bitwise blend
+      // under a lane mask (a select of two elements would be folded into a
+      // runtime index into pm, which costs a compare chain per element)
+      const uint32_t upper = (lane & off) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int i = 0; i < nr / 2; ++i) {
-        const uint32_t send = upper ? pm[i] : pm[i + nr / 2];
-        const uint32_t keep = upper ? pm[i + nr / 2] : pm[i];
+      for (int i = 0; i < half; ++i) {
+        const uint32_t diff = pm[i] ^ pm[i + half];
+        const uint32_t keep = pm[i] ^ (diff & upper);
+        const uint32_t send = keep ^ diff;
         pm[i] = max(keep, uint32_t(__shfl_xor(int(send), off)));
       }
-      nr /= 2;
     } else {
       pm[0] = max(pm[0], uint32_t(__shfl_xor(int(pm[0]), off)));
     }

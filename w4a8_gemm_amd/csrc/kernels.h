@@ -94,9 +94,9 @@ hipError_t launch_w4a16_skinny(const Gemm16Params& p, int gpb, const SkinnyConfi
 constexpr int kFusedMaxRows = 16;
 // Automatic choice (graph-replay timings on MI355X over the Llama-3-8B
 // decode layers): every workgroup quantizes all M x K activations, about
-// five vector instructions per element, which costs more than the launch it
-// saves from 32768 elements on (M = 8 at K = 4096, M = 4 at K = 14336);
-// below that the fused layer is 0.4-2 us faster.  The persistent grid holds
+// four vector instructions per element, which costs more than the launch it
+// saves beyond 32768 elements (M = 16 at K = 4096, M = 4 at K = 14336);
+// up to there the fused layer is 0.3-2 us faster.  The persistent grid holds
 // one workgroup per compute unit (256 on MI355X): wide layers (gate+up,
 // 896 column-tile groups) then quantize A 256 times instead of 896.
 constexpr long kFusedAutoElems = 32768;
