@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 # ------------------------------------------------------------ activation quantizer
 @pytest.mark.parametrize("m,k", [(1, 4096), (16, 14336), (37, 1000), (5, 8), (3, 7),
-                                 (64, 4096), (2, 24576), (300, 136)])
+                                 (64, 4096), (2, 24576), (300, 136),
+                                 (3, 16392), (4, 32768), (2, 32776)])   # 16-chunk rows and past them
 def test_quant_act_bit_exact(m, k):
     a = synth.activations(m, k, seed=m * 7 + k)
     log(f"quant_act m={m} k={k}")

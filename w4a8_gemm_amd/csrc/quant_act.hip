@@ -2,9 +2,10 @@
 //
 // One workgroup (4 waves) per token row.  The row's absolute maximum comes
 // from comparing fp16 bit patterns with the sign cleared (monotone for finite
-// values).  Rows of up to 16384 halves are loaded once into registers, all
-// loads in flight together, and quantized from there; longer rows are read
-// twice (the second pass hits the cache).
+// values).  Rows of up to 32768 halves are loaded once into registers (up to
+// 16 chunks of 8 halves per thread), all loads in flight together, and
+// quantized from there; longer rows are read twice (the second pass hits the
+// cache).
 //
 // The arithmetic (scale, reciprocal, rounding, clamp) is in quant_common.h,
 // shared with the fused small-M GEMM.
@@ -141,6 +142,7 @@ hipError_t launch_quant_act(const uint16_t* a, int m, int k, int lda, int8_t* a8
     if (chunks <= 2) fn = reinterpret_cast<const void*>(&quant_act_kernel<true, 2>);
     else if (chunks <= 4) fn = reinterpret_cast<const void*>(&quant_act_kernel<true, 4>);
     else if (chunks <= 8) fn = reinterpret_cast<const void*>(&quant_act_kernel<true, 8>);
+    else if (chunks <= 16) fn = reinterpret_cast<const void*>(&quant_act_kernel<true, 16>);
     else fn = reinterpret_cast<const void*>(&quant_act_kernel<true, 0>);
   }
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
