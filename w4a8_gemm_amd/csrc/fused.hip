@@ -20,18 +20,25 @@
 // shuffle reduction leaves each lane with one row); every lane derives the
 // s_a and fp32(1 / s_a) of one row as the standalone quantizer does (the same
 // device functions, so the same bits), so all rows take their divisions at
-// once, and each wave writes its int8 rows to its LDS slab, from which the K
-// loop reads the MFMA A operands.  Workgroup 0 also stores A8 and s_a.
+// once, and each wave writes its int8 rows to its own LDS slab, from which
+// its K loop reads the MFMA A operands: no workgroup barrier between the
+// quantization and the K loop.  The epilogue takes s_a from the lanes that
+// derived it.  Workgroup 0 also stores A8 and s_a.
 //
-// Weight ring: slot j = v % D holds block v of the wave's range; once block
-// v has been multiplied the slot is refilled with block v + D, which past the
-// end of the range is block v + D - KBW of the next tile group, so the
-// stream does not drain between groups.  Blocks past the wave's real range
+// All loops over the kw waves (the row maxima, the split-K sum) read LDS at
+// clamped indices without branches, so their reads are issued together.
+//
+// Weight ring of D = 4 slots: slot j = v % D holds block v of the wave's
+// range; once block v has been multiplied the slot is refilled with block
+// v + D, which past the end of the range is block v + D - KBW of the next
+// tile group, so the stream does not drain between groups.  (A ring holding
+// the whole range stalls the prologue: the wave cannot issue that many loads
+// at once and waits at the issue.)  Blocks past the wave's real range
 // (the last wave, when K does not fill kw * KBW blocks) are loaded clamped to
 // its last real block (a cache hit) and not multiplied.
 //
-// LDS: [kw][16] uint32 row maxima, [16] float s_a, [2][kw][NC][256] int32
-// partial tiles when kw > 1 (the halves alternate between tile groups, so one
+// LDS: [kw][16] uint32 row maxima, [2][kw][NC][256] int32 partial tiles
+// when kw > 1 (the halves alternate between tile groups, so one
 // barrier per group suffices), then [kw][M][slab] int8 rows with
 // slab = KBW * 128 + 16 bytes (the pad staggers rows over the banks).
 
@@ -69,10 +76,9 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
   constexpr int slab = KBW * 128 + 16;
 
   uint32_t* amax_lds = reinterpret_cast<uint32_t*>(lds);
-  float* sa_lds = reinterpret_cast<float*>(lds + kw * 64);
-  int32_t* red = reinterpret_cast<int32_t*>(lds + kw * 64 + 64);
+  int32_t* red = reinterpret_cast<int32_t*>(lds + kw * 64);
   const int red_bytes = kw > 1 ? 2 * kw * NC * 1024 : 0;
-  int8_t* my_slab = reinterpret_cast<int8_t*>(lds + kw * 64 + 64 + red_bytes) + wk * p.m * slab;
+  int8_t* my_slab = reinterpret_cast<int8_t*>(lds + kw * 64 + red_bytes) + wk * p.m * slab;
 
   constexpr int MSTEP = GPB <= 0 ? D : 4 / GPB;   // ring slots per meta dword
   u32x4 q[D][NC];
@@ -120,16 +126,32 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
                                          : uint4{0, 0, 0, 0};
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
+  // s1 of a group is loaded one group ahead (raw bits, converted where the
+  // epilogue uses them), so its latency never reaches the epilogue
   const int tg0 = blockIdx.x;
+  uint16_t s1_next[NC];
+  auto load_s1 = [&](int tg) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) s1_next[c] = p.s1[min((tg * NC + c) * 16 + r16, p.n - 1)];
+  };
+  load_s1(tg0);
+  // every wave's activation loads enter the memory pipeline ahead of any
+  // weight load (else a late wave's rows queue behind the others' weights
+  // and the workgroup waits for them at the row-maxima barrier)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < D; ++j) issue(j, tg0, j);
   __builtin_amdgcn_sched_barrier(0);
   // Row maxima, all rows at once: each lane starts with its partial maximum
   // of every row; a transposed butterfly halves the rows a lane holds at each
-  // of the first log2(MF) exchange steps (the lanes with the offset bit set
-  // keep the upper half), so afterwards lane l holds row l / (64 / MF), and
-  // the remaining steps reduce over the lanes that share a row.
+  // of the first log2(MF) exchange steps (the lanes with the step's lane bit
+  // set keep the upper half), so afterwards lane l holds row l / (64 / MF),
+  // and the remaining steps reduce over the lanes that share a row.  The
+  // steps run on the cross-lane paths of the VALU: lane bits 5 and 4 by
+  // the permlane32/permlane16 swaps, bits 3 .. 0 by DPP (row rotate by 8,
+  // half-row mirror, two quad permutes: partners that differ in that bit).
   uint32_t pm[MF];
 #pragma unroll
   for (int r = 0; r < MF; ++r) {
@@ -144,35 +166,50 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
   for (int step = 0; step < 6; ++step) {
     const int off = 32 >> step;
     const int half = (MF >> step) / 2;   // rows handed over at this step (0: none)
-    if (half > 0) {
-      // lanes with the offset bit set keep the upper half: a bitwise blend
-      // under a lane mask (a select of two elements would be folded into a
-      // runtime index into pm, which costs a compare chain per element)
-      const uint32_t upper = (lane & off) ? 0xFFFFFFFFu : 0u;
+    const int n = half > 0 ? half : 1;
 #pragma unroll
-      for (int i = 0; i < half; ++i) {
-        const uint32_t diff = pm[i] ^ pm[i + half];
-        const uint32_t keep = pm[i] ^ (diff & upper);
+    for (int i = 0; i < n; ++i) {
+      const uint32_t x = pm[i], y = half > 0 ? pm[i + half] : pm[i];
+      if (off >= 16) {
+        // the swap leaves lanes without the bit holding (x, partner's x)
+        // and lanes with it (partner's y, y)
+        const auto sw = off == 32 ? __builtin_amdgcn_permlane32_swap(x, y, false, false)
+                                  : __builtin_amdgcn_permlane16_swap(x, y, false, false);
+        pm[i] = max(uint32_t(sw[0]), uint32_t(sw[1]));
+      } else {
+        // lanes with the bit keep y and send x: a bitwise blend under a lane
+        // mask (a select of two elements would be folded into a runtime
+        // index into pm, which costs a compare chain per element)
+        const uint32_t upper = (lane & off) ? 0xFFFFFFFFu : 0u;
+        const uint32_t diff = x ^ y;
+        const uint32_t keep = x ^ (diff & upper);
         const uint32_t send = keep ^ diff;
-        pm[i] = max(keep, uint32_t(__shfl_xor(int(send), off)));
+        constexpr int kDpp[4] = {0xB1, 0x4E, 0x141, 0x128};   // xor 1, xor 2, xor 7, xor 8
+        const int ctrl = kDpp[5 - step];
+        uint32_t got;
+        switch (ctrl) {
+          case 0xB1: got = __builtin_amdgcn_update_dpp(0u, send, 0xB1, 0xF, 0xF, false); break;
+          case 0x4E: got = __builtin_amdgcn_update_dpp(0u, send, 0x4E, 0xF, 0xF, false); break;
+          case 0x141: got = __builtin_amdgcn_update_dpp(0u, send, 0x141, 0xF, 0xF, false); break;
+          default: got = __builtin_amdgcn_update_dpp(0u, send, 0x128, 0xF, 0xF, false); break;
+        }
+        pm[i] = max(keep, got);
       }
-    } else {
-      pm[0] = max(pm[0], uint32_t(__shfl_xor(int(pm[0]), off)));
     }
   }
   constexpr int LPR = 64 / MF;   // lanes per row after the butterfly
   if (lane % LPR == 0) amax_lds[wk * 16 + lane / LPR] = pm[0];
   __syncthreads();
-  // lane l derives the scale of row l % 16 (rows past M have maximum 0)
+  // lane l derives the scale of row l % 16 (rows past M have maximum 0);
+  // the reads repeat the last wave's entry past kw (a maximum is idempotent)
   const bool store_a8 = blockIdx.x == 0;
   uint32_t am = 0;
-  for (int w = 0; w < kw; ++w) am = max(am, r16 < MF ? amax_lds[w * 16 + r16] : 0u);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) am = max(am, amax_lds[min(w, kw - 1) * 16 + r16]);
+  if (r16 >= MF) am = 0;
   const uint16_t sb = act_scale_bits(am);
   const float rc = act_recip(sb);
-  if (wk == 0 && quarter == 0 && r16 < p.m) {
-    sa_lds[r16] = h2f(sb);
-    if (store_a8) p.s_a_out[r16] = sb;
-  }
+  if (store_a8 && wk == 0 && quarter == 0 && r16 < p.m) p.s_a_out[r16] = sb;
 #pragma unroll
   for (int r = 0; r < MF; ++r) {
     if (r >= p.m) continue;   // (not break: the loop must stay unrolled)
@@ -187,11 +224,11 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
       }
     }
   }
-  __syncthreads();   // slabs and s_a visible (each wave reads only its own slab)
-
+  // s_a of the rows this lane stores in the epilogue, from lanes 0 .. 15
+  const float saf = h2f(sb);
   float sa[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sa[r] = sa_lds[min(4 * quarter + r, p.m - 1)];
+  for (int r = 0; r < 4; ++r) sa[r] = __shfl(saf, min(4 * quarter + r, p.m - 1));
 
   // A operand of lane (row r16, k quarter) for block v, half h; rows past M
   // read row M - 1 (their products are never stored)
@@ -231,9 +268,10 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
   // The two copies keep every load unconditional inside the unrolled loop.
   auto run_group = [&](int tg, int tg_next, int it, auto has_next) {
     constexpr bool HAS_NEXT = decltype(has_next)::value;
-    float s1[NC];
+    uint16_t s1_bits[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) s1[c] = h2f(p.s1[min((tg * NC + c) * 16 + r16, p.n - 1)]);
+    for (int c = 0; c < NC; ++c) s1_bits[c] = s1_next[c];
+    if (HAS_NEXT) load_s1(tg_next);
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = v4i{0, 0, 0, 0};
 #pragma unroll
@@ -250,7 +288,7 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
       for (int c = 0; c < NC; ++c) {
         if (tg * NC + c >= ntiles) continue;
         int32_t v[4] = {acc[c][0], acc[c][1], acc[c][2], acc[c][3]};
-        store_frag(p, 0, (tg * NC + c) * 16, lane, v, s1[c], sa);
+        store_frag(p, 0, (tg * NC + c) * 16, lane, v, h2f(s1_bits[c]), sa);
       }
       return;
     }
@@ -262,18 +300,22 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
       for (int r = 0; r < 4; ++r) mine[(c * 4 + r) * 64 + lane] = acc[c][r];
     __syncthreads();
     for (int c = wk; c < NC; c += kw) {
-      if (tg * NC + c >= ntiles) continue;
+      if (tg * NC + c >= ntiles || 4 * quarter >= p.m) continue;
       int32_t v[4] = {0, 0, 0, 0};
-      for (int w = 0; w < kw; ++w) {
-        const int32_t* pp = part + (w * NC + c) * 256;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += pp[r * 64 + lane];
+      for (int w = 0; w < 8; ++w) {
+        const int32_t* pp = part + (min(w, kw - 1) * NC + c) * 256;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t x = pp[r * 64 + lane];
+          v[r] += w < kw ? x : 0;
+        }
       }
-      float s1c = s1[0];
+      uint16_t s1c = s1_bits[0];
 #pragma unroll
       for (int cc = 1; cc < NC; ++cc)
-        if (cc == c) s1c = s1[cc];
-      store_frag(p, 0, (tg * NC + c) * 16, lane, v, s1c, sa);
+        if (cc == c) s1c = s1_bits[cc];
+      store_frag(p, 0, (tg * NC + c) * 16, lane, v, h2f(s1c), sa);
     }
   };
 
@@ -347,7 +389,7 @@ hipError_t fused_by_kbw(const GemmParams& p, const uint16_t* a, int lda, int gpb
 
 size_t fused_lds_bytes(int kw, int nc, int m, int kbw) {
   const size_t red = kw > 1 ? 2 * size_t(kw) * nc * 1024 : 0;
-  return size_t(kw) * 64 + 64 + red + size_t(kw) * m * (size_t(kbw) * 128 + 16);
+  return size_t(kw) * 64 + red + size_t(kw) * m * (size_t(kbw) * 128 + 16);
 }
 
 int fused_rows(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : (m <= 8 ? 8 : 16))); }
