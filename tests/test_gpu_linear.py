@@ -102,10 +102,11 @@ def test_linear_fused_every_shape(n_tiles, k_split, workgroups):
 @pytest.mark.parametrize("m,n,k,g,workgroups", [
     (16, 4112, 4096, 128, 0), (16, 4112, 4096, 128, 100), (11, 1040, 4096, 64, 7),
     (4, 4096, 14336, 128, 0), (8, 2064, 8192, 128, 50), (13, 272, 2048, 1, 3),
-    (2, 6144, 4096, 1, 0)])
+    (2, 6144, 4096, 1, 0), (4, 528, 16384, 0, 0), (3, 1040, 8192, 64, 0)])
 def test_linear_fused_up_to_16_rows(m, n, k, g, workgroups):
-    """Up to 16 tokens, long wave ranges (16 blocks), codebook weights, and
-    persistent grids: A8, s_a and acc bit-exact with the oracle."""
+    """Up to 16 tokens, long wave ranges (16 blocks; per-row groups over 2048 k
+    per wave, the widest partial sums), codebook weights, and persistent
+    grids: A8, s_a and acc bit-exact with the oracle."""
     w = synth.weights(n, k, seed=131 + m, dist="student_t4")
     a = synth.activations(m, k, seed=132 + m)
     assert _fused_applies(m, n, k, g, workgroups=workgroups)

@@ -37,6 +37,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// v_mul_i32_i24: the product of the low 24 bits of a and b, read as signed
+// integers (the LLVM intrinsic, reached through its symbol name).  Exact when
+// both factors lie in [-2^23, 2^23); a full-rate instruction, where a 32-bit
+// multiply takes four issue cycles.
+extern "C" __device__ int w4a8_mul_i24(int a, int b) __asm("llvm.amdgcn.mul.i24");
+
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
   u16x2 va = __builtin_bit_cast(u16x2, a);
   u16x2 vb = __builtin_bit_cast(u16x2, b);
