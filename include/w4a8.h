@@ -201,8 +201,9 @@ w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
 /* ------------------------------------------------------------ whole layer
  * The W4A8 linear layer from fp16 activations: per-token quantization of A
  * (as w4a8_quant_act) followed by the GEMM (as w4a8_gemm), with A8 and s_a
- * written to a8_dev / s_a_dev as well.  For up to 32768 activations
- * (m * k; e.g. up to 8 tokens at k = 4096) both steps run in one kernel:
+ * written to a8_dev / s_a_dev as well.  For up to 57344 activations
+ * (m * k; e.g. up to 14 tokens at k = 4096, 4 at k = 14336), or 65536 on
+ * layers of at least 16384 columns, both steps run in one kernel:
  * each workgroup of a persistent grid quantizes the rows itself while its
  * first weight loads are in flight, then walks several column tiles, which
  * saves a launch and a round trip of A8 through memory; otherwise it makes

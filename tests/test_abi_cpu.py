@@ -315,8 +315,9 @@ def test_linear_validates_before_any_hip_call():
 
 
 def test_linear_launch_plan():
-    """w4a8_linear_launches: one fused launch up to 32768 activations
-    (M x K) where the fused kernel applies, two otherwise, three when the
+    """w4a8_linear_launches: one fused launch up to 57344 activations
+    (M x K), 65536 on layers of 16384 columns or more, where the fused
+    kernel applies, two otherwise, three when the
     GEMM splits K over workgroups; forced, the fused kernel takes up to 16
     tokens (rows x k-blocks per wave within its budget, wave ranges of at
     most 16 blocks)."""
@@ -327,10 +328,13 @@ def test_linear_launch_plan():
     assert L.w4a8_linear_launches(4, 4096, 4096, 128, None) == 1
     assert L.w4a8_linear_launches(2, 4096, 14336, 128, None) == 1
     assert L.w4a8_linear_launches(2, 256, 1024, 1, None) == 1         # codebook weights
-    assert L.w4a8_linear_launches(8, 4096, 4096, 128, None) == 1      # 32768 activations
-    assert L.w4a8_linear_launches(9, 4096, 4096, 128, None) == 2
-    assert L.w4a8_linear_launches(4, 4096, 14336, 128, None) == 2
+    assert L.w4a8_linear_launches(8, 4096, 4096, 128, None) == 1
+    assert L.w4a8_linear_launches(14, 4096, 4096, 128, None) == 1     # 57344 activations
+    assert L.w4a8_linear_launches(15, 4096, 4096, 128, None) == 2
+    assert L.w4a8_linear_launches(4, 4096, 14336, 128, None) == 1
     assert L.w4a8_linear_launches(16, 4096, 4096, 128, None) == 2
+    assert L.w4a8_linear_launches(16, 16384, 4096, 128, None) == 1    # wide: 65536 activations
+    assert L.w4a8_linear_launches(16, 16368, 4096, 128, None) == 2
     assert L.w4a8_linear_launches(17, 4096, 4096, 128, None) == 2
     assert L.w4a8_linear_launches(256, 4096, 14336, 128, None) == 3
     assert L.w4a8_linear_launches(1, 4096, 131072, 128, None) == 2    # K range too long to fuse

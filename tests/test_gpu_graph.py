@@ -42,10 +42,11 @@ def test_graph_replays_match_eager(m, n, k, g):
 
 
 @pytest.mark.parametrize("m,n,k,g", [(1, 4096, 4096, 128), (2, 6144, 4096, 32), (4, 4096, 14336, 128),
-                                     (16, 6144, 4096, 128), (256, 4096, 14336, 128),
-                                     (64, 512, 1024, 1), (100, 272, 768, 64)])
+                                     (16, 6144, 4096, 128), (16, 16384, 4096, 128),
+                                     (256, 4096, 14336, 128), (64, 512, 1024, 1), (100, 272, 768, 64)])
 def test_graph_whole_layer_replays_match_eager(m, n, k, g):
-    """w4a8_linear (fused for 1-2 tokens, quantizer + GEMM otherwise, K split
+    """w4a8_linear (fused up to 4 tokens here and at 16 tokens on 16384
+    columns, quantizer + GEMM at 16 tokens on 6144 columns, K split
     through a workspace at M = 256, codebook weights) inside a captured graph:
     every replay, with eager work and synchronizations in between, equals
     the eager result."""

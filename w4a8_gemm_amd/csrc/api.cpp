@@ -271,11 +271,10 @@ namespace {
 // waves with 4, 8 or 16 blocks each (every wave kept, as for the skinny
 // kernel); a persistent grid of kFusedAutoWgs workgroups unless forced.
 SkinnyConfig fused_plan(int m, int n, int k, const w4a8_gemm_opts* opts) {
-  (void)m;
   SkinnyConfig c{};
   c.mr = 1;
   const int kblocks = k / kKBlock;
-  c.nc = n / kColTile <= 256 ? 1 : 2;
+  c.nc = n / kColTile > kFusedPairTiles && m > 2 ? 2 : 1;
   c.kw = std::min(8, std::max(1, kblocks / 4));
   if (opts && opts->k_split > 0) c.kw = opts->k_split;
   const int per = (kblocks + c.kw - 1) / c.kw;
@@ -287,8 +286,11 @@ SkinnyConfig fused_plan(int m, int n, int k, const w4a8_gemm_opts* opts) {
 }
 
 // The automatic choice runs the fused kernel wherever it applies for up to
-// kFusedAutoElems activations.
-bool fused_by_default(int m, int k) { return long(m) * k <= kFusedAutoElems; }
+// kFusedAutoElems activations, kFusedWideElems on wide layers.
+bool fused_by_default(int m, int n, int k) {
+  const long elems = long(m) * k;
+  return elems <= kFusedAutoElems || (elems <= kFusedWideElems && n / kColTile >= kFusedWideTiles);
+}
 
 }  // namespace
 
@@ -313,7 +315,7 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
   const SkinnyConfig fc = fused_plan(m, n, k, opts);
   const bool fused_ok = fused_config_supported(fc, m, k);
   if (variant == 3 && !fused_ok) return W4A8_ERR_UNSUPPORTED;
-  if (variant == 3 || (variant == 0 && fused_ok && fused_by_default(m, k))) {
+  if (variant == 3 || (variant == 0 && fused_ok && fused_by_default(m, n, k))) {
     Sections sec = sections(n, k, g);
     const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
     GemmParams p{};
@@ -389,7 +391,7 @@ extern "C" int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_
   if (variant < 0 || variant > 3 || (opts && opts->workgroups < 0)) return 0;
   const bool fused_ok = fused_config_supported(fused_plan(m, n, k, opts), m, k);
   if (variant == 3) return fused_ok ? 1 : 0;
-  if (variant == 0 && fused_ok && fused_by_default(m, k)) return 1;
+  if (variant == 0 && fused_ok && fused_by_default(m, n, k)) return 1;
   return plan_gemm(m, n, k, opts).slices > 1 ? 3 : 2;
 }
 

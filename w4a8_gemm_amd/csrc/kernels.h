@@ -95,11 +95,18 @@ constexpr int kFusedMaxRows = 16;
 // Automatic choice (graph-replay timings on MI355X over the Llama-3-8B
 // decode layers): every workgroup quantizes all M x K activations, about
 // four vector instructions per element, which costs more than the launch it
-// saves beyond 32768 elements (M = 16 at K = 4096, M = 4 at K = 14336);
-// up to there the fused layer is 0.3-2 us faster.  The persistent grid holds
-// one workgroup per compute unit (256 on MI355X): wide layers (gate+up,
-// 896 column-tile groups) then quantize A 256 times instead of 896.
-constexpr long kFusedAutoElems = 32768;
+// saves beyond 57344 elements (M = 14 at K = 4096, M = 4 at K = 14336; up
+// to there the fused layer is 0.1-3 us faster), or beyond 65536 elements on
+// layers of at least kFusedWideTiles column tiles, whose workgroups walk
+// several tile groups and so quantize once for more weights (gate+up at
+// M = 16: 16.6 against 18.0 us).  The persistent grid holds one workgroup
+// per compute unit (256 on MI355X).  Groups hold one column tile, except on
+// layers of more than kFusedPairTiles tiles above 2 tokens, where two tiles
+// per group halve the per-group split-K sums and barriers.
+constexpr long kFusedAutoElems = 57344;
+constexpr long kFusedWideElems = 65536;
+constexpr int kFusedWideTiles = 1024;
+constexpr int kFusedPairTiles = 512;
 constexpr int kFusedAutoWgs = 256;
 constexpr int kFusedMaxHold = 64;
 constexpr size_t kFusedMaxLds = 128 * 1024;
