@@ -237,31 +237,17 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
   v4i sacc;   // per-row groups: row sums of A8 over the wave's range
 
   // Groups that cover whole MFMA steps (a 128-k block, a 64-k half, or the
-  // row) are factored: the MFMA multiplies the raw codes q, and the group's
-  // zero point and step enter as s2 * (sum a * q - z * sum a) over the group,
-  // an integer identity with sum a * (q - z) * s2, so the int32 sums are the
-  // same.  The row sums of A come from one more MFMA against a B operand of
-  // ones, shared by the NC tiles.  The codes need 3 vector instructions per
-  // 8 weights instead of 7, plus 3 per output value and group.
+  // row; a wave's range spans at most 2048 k) are factored out of the inner
+  // product: raw codes into the MFMA, s2 * (sum a * q - z * sum a) per group,
+  // the row sums from one more MFMA against ones, shared by the NC tiles.
+  // The codes need 3 vector instructions per 8 weights instead of 7, plus 3
+  // per output value and group.  Only the values that can hold a row below
+  // MF are corrected: with MF <= 4 the valid rows are values 0 .. MF-1 of
+  // lanes 0 .. 15, and the rest are never stored.
   constexpr bool FACTORED = GPB == 0 || GPB == 1 || GPB == 2;
+  constexpr int NV = MF < 4 ? MF : 4;
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  auto codes = [&](const u32x4& qc, int h) {
-    const uint32_t w0 = h ? qc.z : qc.x;
-    const uint32_t w1 = h ? qc.w : qc.y;
-    return v4i{int(w0 & 0x0F0F0F0Fu), int((w0 >> 4) & 0x0F0F0F0Fu), int(w1 & 0x0F0F0F0Fu),
-               int((w1 >> 4) & 0x0F0F0F0Fu)};
-  };
-  // acc += s2 * (g - z * s) for the group of meta byte mb, in 24-bit
-  // products: |s|, |g - z * s| < 2^23 (a group or a wave's range spans at
-  // most 2048 k, and |a|, q, z <= 127, 15, 15).  Only the values that can
-  // hold a row below MF are corrected: with MF <= 4 the valid rows are
-  // values 0 .. MF-1 of lanes 0 .. 15, and the rest are never stored.
-  auto add_group = [&](v4i& a, const v4i& g, const v4i& sm, uint32_t mb) {
-    const int s2 = int(mb >> 4) + 1, z = int(mb & 15u);
-#pragma unroll
-    for (int i = 0; i < (MF < 4 ? MF : 4); ++i)
-      a[i] += w4a8_mul_i24(s2, g[i] - w4a8_mul_i24(z, sm[i]));
-  };
+  auto codes = [&](const u32x4& qc, int h) { return h ? codes16(qc.z, qc.w) : codes16(qc.x, qc.y); };
 
   // decode block v from ring slot j = v % D and multiply it into acc
   auto compute = [&](int j, int v) {
@@ -286,7 +272,7 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
         for (int c = 0; c < NC; ++c) {
           v4i g = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0], codes(qs[c], 0), v4i{0, 0, 0, 0}, 0, 0, 0);
           g = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1], codes(qs[c], 1), g, 0, 0, 0);
-          add_group(acc[c], g, sm, (ms[c] >> (8 * (v & 3))) & 0xFFu);
+          add_group<NV>(acc[c], g, sm, (ms[c] >> (8 * (v & 3))) & 0xFFu);
         }
       } else {
 #pragma unroll
@@ -296,7 +282,7 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
           for (int c = 0; c < NC; ++c) {
             const v4i g =
                 __builtin_amdgcn_mfma_i32_16x16x64_i8(af[h], codes(qs[c], h), v4i{0, 0, 0, 0}, 0, 0, 0);
-            add_group(acc[c], g, sm, (ms[c] >> (8 * (2 * (v & 1) + h))) & 0xFFu);
+            add_group<NV>(acc[c], g, sm, (ms[c] >> (8 * (2 * (v & 1) + h))) & 0xFFu);
           }
         }
       }
@@ -355,7 +341,7 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
       for (int c = 0; c < NC; ++c) {
         const v4i raw = acc[c];
         acc[c] = v4i{0, 0, 0, 0};
-        add_group(acc[c], raw, sacc, row_meta[c] & 0xFFu);
+        add_group<NV>(acc[c], raw, sacc, row_meta[c] & 0xFFu);
       }
     }
     if (kw == 1) {

@@ -79,6 +79,29 @@ __device__ __forceinline__ v4i decode16(uint32_t w0, uint32_t w1, GroupConst g) 
   return b;
 }
 
+// Groups that cover whole MFMA steps (a 128-k block, a 64-k half, or the
+// row) can be factored out of the inner product: the MFMA multiplies the raw
+// codes q, and the group enters as s2 * (sum a * q - z * sum a), an integer
+// identity with sum a * (q - z) * s2, so the int32 sums are the same.  The
+// row sums of A come from an MFMA against a B operand of ones.
+
+// Two packed words (16 codes) -> the raw codes as one B operand, in the k
+// order of decode16.
+__device__ __forceinline__ v4i codes16(uint32_t w0, uint32_t w1) {
+  return v4i{int(w0 & 0x0F0F0F0Fu), int((w0 >> 4) & 0x0F0F0F0Fu), int(w1 & 0x0F0F0F0Fu),
+             int((w1 >> 4) & 0x0F0F0F0Fu)};
+}
+
+// acc[0 .. NV) += s2 * (g - z * s) for the group of meta byte mb, in 24-bit
+// products: valid while |s|, |g - z * s| < 2^23, i.e. for groups of up to
+// 2048 k (|a|, q, z <= 127, 15, 15).
+template <int NV>
+__device__ __forceinline__ void add_group(v4i& acc, const v4i& g, const v4i& s, uint32_t mb) {
+  const int s2 = int(mb >> 4) + 1, z = int(mb & 15u);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] += w4a8_mul_i24(s2, g[i] - w4a8_mul_i24(z, s[i]));
+}
+
 // Epilogue scales of one lane, fetched at kernel start so that the final
 // stores do not wait on a dependent global load.
 template <int MR, int NC>
