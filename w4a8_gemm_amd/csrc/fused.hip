@@ -28,12 +28,14 @@
 // All loops over the kw waves (the row maxima, the split-K sum) read LDS at
 // clamped indices without branches, so their reads are issued together.
 //
-// Weight ring of D = 4 slots: slot j = v % D holds block v of the wave's
-// range; once block v has been multiplied the slot is refilled with block
-// v + D, which past the end of the range is block v + D - KBW of the next
-// tile group, so the stream does not drain between groups.  (A ring holding
-// the whole range stalls the prologue: the wave cannot issue that many loads
-// at once and waits at the issue.)  Blocks past the wave's real range
+// Weight ring of D slots (4, or 8 for ranges of 8 or 16 blocks): slot
+// j = v % D holds block v of the wave's range; once block v has been
+// multiplied the slot is refilled with block v + D, which past the end of
+// the range is block v + D - KBW of the next tile group, so the stream does
+// not drain between groups.  The first 4 slots are issued before the
+// prologue, the rest after its row-maxima barrier: a wave cannot issue many
+// more loads at once and would stall at the issue, delaying its own
+// prologue (a 16-slot ring did).  Blocks past the wave's real range
 // (the last wave, when K does not fill kw * KBW blocks) are loaded clamped to
 // its last real block (a cache hit) and not multiplied.
 //
@@ -141,8 +143,9 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+  constexpr int D0 = D < 4 ? D : 4;   // slots issued before the prologue
 #pragma unroll
-  for (int j = 0; j < D; ++j) issue(j, tg0, j);
+  for (int j = 0; j < D0; ++j) issue(j, tg0, j);
   __builtin_amdgcn_sched_barrier(0);
   // Row maxima, all rows at once: each lane starts with its partial maximum
   // of every row; a transposed butterfly halves the rows a lane holds at each
@@ -200,6 +203,8 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
   constexpr int LPR = 64 / MF;   // lanes per row after the butterfly
   if (lane % LPR == 0) amax_lds[wk * 16 + lane / LPR] = pm[0];
   __syncthreads();
+#pragma unroll
+  for (int j = D0; j < D; ++j) issue(j, tg0, j);
   // lane l derives the scale of row l % 16 (rows past M have maximum 0);
   // the reads repeat the last wave's entry past kw (a maximum is idempotent)
   const bool store_a8 = blockIdx.x == 0;
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
 template <int NC, int GPB, int MF, int KBW>
 hipError_t launch_fused_t(const GemmParams& p, const uint16_t* a, int lda, const SkinnyConfig& c,
                           hipStream_t stream) {
-  constexpr int D = 4;
+  constexpr int D = KBW >= 8 ? 8 : 4;
   const void* fn = reinterpret_cast<const void*>(&fused_kernel<NC, GPB, D, MF, KBW>);
   const size_t lds = fused_lds_bytes(c.kw, NC, p.m, KBW);
   if (lds > 65536) {
