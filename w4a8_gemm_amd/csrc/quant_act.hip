@@ -24,9 +24,8 @@ using namespace dev;
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t row_absmax_bits(uint32_t mx, int tid) {
-  uint32_t m16 = absmax_bits(mx);
   // wave reduction, then across the four waves through LDS
-  for (int off = 32; off > 0; off >>= 1) m16 = max(m16, uint32_t(__shfl_xor(int(m16), off)));
+  const uint32_t m16 = wave_max_u32(absmax_bits(mx));
   __shared__ uint32_t wave_max[kThreads / 64];
   if ((tid & 63) == 0) wave_max[tid >> 6] = m16;
   __syncthreads();

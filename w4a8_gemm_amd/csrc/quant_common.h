@@ -47,6 +47,23 @@ __device__ __forceinline__ uint16_t act_scale_bits(uint32_t amax_bits) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(amax / 127.0f));
 }
 
+// Maximum of x over the 64 lanes of a wave, in every lane, on the VALU's
+// cross-lane paths (no LDS round trip): lane bits 5 and 4 by the permlane32 /
+// permlane16 swaps (each leaves a lane and its partner's value in the two
+// results), bits 3 .. 0 by DPP (row rotate by 8, half-row mirror, two quad
+// permutes: partners that differ in that bit).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = max(uint32_t(s32[0]), uint32_t(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(uint32_t(s16[0]), uint32_t(s16[1]));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false)));
+  return x;
+}
+
 // the multiplier fp32(1 / s_a), 0 for a zero row
 __device__ __forceinline__ float act_recip(uint16_t scale_bits) {
   const float scale = h2f(scale_bits);
