@@ -14,10 +14,11 @@
 // per group.  Partial int32 tiles of the waves are summed exactly through LDS.
 //
 // Prologue: each wave loads its K range of rows 0 .. M-1 (fp16, 16-byte
-// chunks spread over all 64 lanes) into registers; the weight ring of the
-// first tile group is issued right behind those loads, so the weight stream
-// starts at once.  The waves' partial row maxima meet in LDS (a transposed
-// shuffle reduction leaves each lane with one row); every lane derives the
+// chunks spread over all 64 lanes) into registers; after a barrier that puts
+// every wave's activation loads ahead of any weight load, the weight ring of
+// the first tile group is issued, so the weight stream starts at once.  The
+// waves' partial row maxima meet in LDS (a transposed butterfly on the
+// VALU's cross-lane paths leaves each lane with one row); every lane derives the
 // s_a and fp32(1 / s_a) of one row as the standalone quantizer does (the same
 // device functions, so the same bits), so all rows take their divisions at
 // once, and each wave writes its int8 rows to its own LDS slab, from which
@@ -27,6 +28,11 @@
 //
 // All loops over the kw waves (the row maxima, the split-K sum) read LDS at
 // clamped indices without branches, so their reads are issued together.
+//
+// K loop: groups of whole MFMA steps (g = 128, g = 64, per row) are factored
+// out of the inner product (raw codes into the MFMA, one correction per
+// group and output value); g = 32 and codebook weights are decoded to int8
+// operands first.
 //
 // Weight ring of D slots (4, or 8 for ranges of 8 or 16 blocks): slot
 // j = v % D holds block v of the wave's range; once block v has been
