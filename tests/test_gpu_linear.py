@@ -119,6 +119,24 @@ def test_linear_fused_up_to_16_rows(m, n, k, g, workgroups):
     assert ref.y_tolerance_ok(y, out["y"]).all()
 
 
+@pytest.mark.parametrize("m,n,k,g", [(16, 16400, 4096, 128), (3, 8208, 4096, 64)])
+def test_linear_auto_paired_tiles_ragged(m, n, k, g):
+    """The automatic plan's two column tiles per group (layers of more than
+    512 tiles above 2 tokens; 16 tokens only on 1024+ tiles) with an odd tile
+    count, so the last group holds one tile: one fused launch, bit-exact
+    with the oracle."""
+    assert int(w4.lib.w4a8_linear_launches(m, n, k, g, None)) == 1
+    w = synth.weights(n, k, seed=151 + m, dist="student_t4")
+    a = synth.activations(m, k, seed=152 + m)
+    out = ref.linear(a, w, g)
+    log(f"linear auto paired tiles m={m} n={n} k={k} g={g}")
+    y, a8, s_a, acc = _run_linear(a, w4.pack(w, g), n, k, g)
+    assert np.array_equal(s_a.view(np.uint16), out["s_a"].view(np.uint16))
+    assert np.array_equal(a8, out["a8"])
+    assert np.array_equal(acc, out["acc"])
+    assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
 def test_linear_fused_rounding_ties():
     """Rows built so that A * (1 / s_a) lands on every half-integer and near
     the clamp: s_a = 1 (absmax 127), 2 (absmax 254) and an inexact scale."""
