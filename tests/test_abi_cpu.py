@@ -337,6 +337,8 @@ def test_linear_launch_plan():
     assert L.w4a8_linear_launches(16, 16368, 4096, 128, None) == 2
     assert L.w4a8_linear_launches(17, 4096, 4096, 128, None) == 2
     assert L.w4a8_linear_launches(256, 4096, 14336, 128, None) == 3
+    assert L.w4a8_linear_launches(64, 4096, 14336, 128, None) == 3    # 17..64 tokens, long K
+    assert L.w4a8_linear_launches(24, 4096, 14336, 128, None) == 2    # below 393216 activations
     assert L.w4a8_linear_launches(1, 4096, 131072, 128, None) == 2    # K range too long to fuse
     opts = w4.GemmOpts(3)
     assert L.w4a8_linear_launches(16, 4096, 4096, 128, ctypes.byref(opts)) == 1

@@ -137,6 +137,23 @@ def test_linear_auto_paired_tiles_ragged(m, n, k, g):
     assert ref.y_tolerance_ok(y, out["y"]).all()
 
 
+@pytest.mark.parametrize("m,n,k,g", [(64, 4096, 14336, 128), (33, 1040, 16384, 64),
+                                     (48, 2048, 8192, 0), (40, 528, 12288, 32)])
+def test_linear_auto_small_m_k_split(m, n, k, g):
+    """17..64 tokens with long K: the automatic plan splits K over
+    workgroups of 64 x 128 tiles (quantizer, GEMM, reduction); ragged column
+    tiles, per-row and 32-wide groups; bit-exact with the oracle."""
+    assert int(w4.lib.w4a8_linear_launches(m, n, k, g, None)) == 3
+    w = synth.weights(n, k, seed=171 + m, dist="student_t4")
+    a = synth.activations(m, k, seed=172 + m)
+    out = ref.linear(a, w, g)
+    log(f"linear auto split m={m} n={n} k={k} g={g}")
+    y, a8, s_a, acc = _run_linear(a, w4.pack(w, g), n, k, g)
+    assert np.array_equal(a8, out["a8"])
+    assert np.array_equal(acc, out["acc"])
+    assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
 def test_linear_fused_rounding_ties():
     """Rows built so that A * (1 / s_a) lands on every half-integer and near
     the clamp: s_a = 1 (absmax 127), 2 (absmax 254) and an inexact scale."""

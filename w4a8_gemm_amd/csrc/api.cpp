@@ -124,11 +124,15 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   Plan pl;
   pl.variant = opts ? opts->variant : 0;
   if (pl.variant < 0 || pl.variant > 2) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
+  const int kblocks = k / kKBlock;
   // the skinny kernel up to 16 tokens, and up to 64 unless the layer is
   // wide enough to give the tiled kernel's 64 x 128 tiles most of the GPU
-  // (its activation fragments, re-read by every workgroup, grow with M)
-  if (pl.variant == 0) pl.variant = (m <= 16 || (m <= 64 && tiled_tiles(m, n, 64, 128) < 192)) ? 1 : 2;
-  const int kblocks = k / kKBlock;
+  // (its activation fragments, re-read by every workgroup, grow with M), or
+  // K is long enough that those re-reads (M * K bytes per workgroup) cost
+  // more than splitting K over workgroups
+  const bool split_small = m > 16 && m <= 64 && kblocks >= 64 && long(m) * k >= kSplitSmallElems;
+  if (pl.variant == 0)
+    pl.variant = (m <= 16 || (m <= 64 && tiled_tiles(m, n, 64, 128) < 192 && !split_small)) ? 1 : 2;
   if (pl.variant == 1) {
     if (m > 64) { pl.status = W4A8_ERR_UNSUPPORTED; return pl; }
     SkinnyConfig& c = pl.skinny;
@@ -145,6 +149,8 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   // waves, or two of four, per compute unit, so the tile shrinks with the
   // grid it yields:
   //   >= 224 tiles of 256 x 256          -> 256 x 256, eight waves, 3 stages
+  //   M <= 64, K >= 8192, < 192 of 64x128 -> 64 x 128 with K split over 2..16
+  //                                         workgroups (~256 in all)
   //   K >= 8192 and < 192 of 128 x 256   -> 128 x 256 with K split over
   //                                         2..8 workgroups (~384 in all)
   //   >= 256 tiles of 128 x 128, M > 64 -> 128 x 128, four waves, 3 stages
@@ -174,6 +180,12 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     if (opts->n_tiles > 0) c.nc = opts->n_tiles;
   } else if (t256 >= 224) {
     c = TiledConfig{8, 4, 4, 2, 1, 3};
+  } else if (m <= 64 && kblocks >= 64 && tiled_tiles(m, n, 64, 128) < 192) {
+    // 17..64 tokens, long K: 64 x 128 tiles, K split so that ~256
+    // workgroups run (each slice re-reads only its part of A8)
+    c = TiledConfig{4, 2, 4, 1, 1, 3};
+    const long want = 256 / tiled_tiles(m, n, 64, 128);
+    slices = int(std::max(2L, std::min<long>(want, kMaxSlices)));
   } else if (kblocks >= 64 && t128x256 < 192) {
     c = TiledConfig{8, 4, 4, 1, 1, 2};
     const long want = (384 + t128x256 - 1) / t128x256;

@@ -28,6 +28,12 @@ struct GemmParams {
 };
 
 constexpr int kMaxSlices = 16;   // workgroups splitting K of one tile
+// 17..64 tokens with K >= 8192: from this many activations (M * K) on, 64 x
+// 128 tiles with K split over workgroups beat the skinny kernel, whose every
+// workgroup re-reads all of A8 (graph replays on MI355X: down projection
+// 4096 x 14336 at M = 64 22.5 against 35.1 us, M = 32 20.6 against 21.7;
+// 8192 x 8192 at M = 48 20.7 against 21.9, M = 32 20.0 against 16.8)
+constexpr long kSplitSmallElems = 393216;
 
 // W4A16 comparison GEMM on the same blob: fp16 activations, fp16 output.
 struct Gemm16Params {
