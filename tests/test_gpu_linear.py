@@ -138,9 +138,9 @@ def test_linear_auto_paired_tiles_ragged(m, n, k, g):
 
 
 @pytest.mark.parametrize("m,n,k,g", [(64, 4096, 14336, 128), (33, 1040, 16384, 64),
-                                     (48, 2048, 8192, 0), (40, 528, 12288, 32)])
+                                     (48, 2048, 8192, 0), (40, 528, 12288, 32), (96, 1040, 8192, 64)])
 def test_linear_auto_small_m_k_split(m, n, k, g):
-    """17..64 tokens with long K: the automatic plan splits K over
+    """17..128 tokens with long K: the automatic plan splits K over
     workgroups of 64 x 128 tiles (quantizer, GEMM, reduction); ragged column
     tiles, per-row and 32-wide groups; bit-exact with the oracle."""
     assert int(w4.lib.w4a8_linear_launches(m, n, k, g, None)) == 3
