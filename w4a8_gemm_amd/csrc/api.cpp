@@ -296,7 +296,9 @@ SkinnyConfig fused_plan(int m, int n, int k, const w4a8_gemm_opts* opts) {
   const int per = (kblocks + c.kw - 1) / c.kw;
   c.kbw = per <= 4 ? 4 : (per <= 8 ? 8 : (per <= 16 ? 16 : 0));
   if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
-  c.wgs = kFusedAutoWgs;
+  const int groups = (n / kColTile + c.nc - 1) / c.nc;
+  const int rounds = (groups + kFusedAutoWgs - 1) / kFusedAutoWgs;
+  c.wgs = (groups + rounds - 1) / rounds;
   if (opts && opts->workgroups != 0) c.wgs = opts->workgroups;
   return c;
 }

@@ -105,8 +105,11 @@ constexpr int kFusedMaxRows = 16;
 // to there the fused layer is 0.1-3 us faster), or beyond 65536 elements on
 // layers of at least kFusedWideTiles column tiles, whose workgroups walk
 // several tile groups and so quantize once for more weights (gate+up at
-// M = 16: 16.6 against 18.0 us).  The persistent grid holds one workgroup
-// per compute unit (256 on MI355X).  Groups hold one column tile, except on
+// M = 16: 16.6 against 18.0 us).  The persistent grid holds at most one
+// workgroup per compute unit (256 on MI355X), and fewer where that evens out
+// the groups each one walks without adding a round: 224 workgroups of 4
+// groups beat 256 of 3 or 4 (gate+up above 2 tokens, 896 groups: 13.4
+// against 13.8 us at M = 4).  Groups hold one column tile, except on
 // layers of more than kFusedPairTiles tiles above 2 tokens, where two tiles
 // per group halve the per-group split-K sums and barriers.
 constexpr long kFusedAutoElems = 57344;
