@@ -175,6 +175,23 @@ def test_linear_fused_rounding_ties():
     assert np.array_equal(acc, out["acc"])
 
 
+@pytest.mark.parametrize("m", [3, 70])
+def test_linear_max_depth(m):
+    """The whole layer at K = W4A8_K_MAX (131072): quantizer rows of 16384
+    chunks, then the skinny (M = 3) or K-split tiled (M = 70) GEMM."""
+    n, k, g = 48, 131072, 64
+    w = synth.weights(n, k, seed=71, dist="student_t4")
+    a = synth.activations(m, k, seed=72 + m)
+    out = ref.linear(a, w, g)
+    blob = w4.pack(w, g)
+    log(f"linear max depth m={m} k={k}")
+    y, a8, s_a, acc = _run_linear(a, blob, n, k, g, variant=0)
+    assert np.array_equal(s_a.view(np.uint16), out["s_a"].view(np.uint16))
+    assert np.array_equal(a8, out["a8"])
+    assert np.array_equal(acc, out["acc"])
+    assert ref.y_tolerance_ok(y, out["y"]).all()
+
+
 def test_linear_strided_rows_and_padding():
     n, k, g, m = 96, 640, 64, 3
     w = synth.weights(n, k, seed=81)

@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 # ------------------------------------------------------------ activation quantizer
 @pytest.mark.parametrize("m,k", [(1, 4096), (16, 14336), (37, 1000), (5, 8), (3, 7),
                                  (64, 4096), (2, 24576), (300, 136),
-                                 (3, 16392), (4, 32768), (2, 32776)])   # 16-chunk rows and past them
+                                 (3, 16392), (4, 32768), (2, 32776),   # 16-chunk rows and past them
+                                 (2, 131072)])                         # the deepest K the GEMM takes
 def test_quant_act_bit_exact(m, k):
     a = synth.activations(m, k, seed=m * 7 + k)
     log(f"quant_act m={m} k={k}")
@@ -266,6 +267,31 @@ def test_gemm_extreme_operands():
     log("gemm extreme operands k=24576")
     y, acc = run_gemm(a8, s_a, blob, n, k, g)
     assert np.array_equal(acc, acc_ref)
+
+
+@pytest.mark.parametrize("m", [1, 5, 80])
+def test_gemm_max_depth_extremes(m):
+    """K = W4A8_K_MAX (131072) with A8 = +-127 against decoded weights of
+    +-120 and +-112: sums reach 127 * 120 * 131072 (about 2.0e9, just under
+    2^31) and must stay exact.  M = 1 and 5 take the skinny kernel with long
+    wave ranges, M = 80 the tiled kernel with K split over workgroups."""
+    n, k, g = 32, 131072, 128
+    w = np.ones((n, k), dtype=np.float32)        # W8 = 119 -> s2 = 8, q = 15: 120
+    w[1::2] = -1.0
+    w[2, 1::2] = -1.0                            # +-119 in one group: s2 = 16, z = 7: +-112
+    blob = w4.pack(w, g)
+    qw = ref.quantize_weights(w, g)
+    w8hat = ref.decoded_weights(qw)
+    assert w8hat[0].min() == 120 and w8hat[2].max() == 112 and w8hat[2].min() == -112
+    a8 = np.full((m, k), 127, dtype=np.int8)
+    a8[1::2] = -127
+    s_a = np.full(m, 2.0 ** -14, dtype=np.float16)
+    acc_ref = ref.gemm_acc(a8, w8hat)
+    assert np.abs(acc_ref).max() == 127 * 120 * k
+    log(f"gemm max depth m={m} k={k}")
+    y, acc = run_gemm(a8, s_a, blob, n, k, g)
+    assert np.array_equal(acc, acc_ref)
+    assert ref.y_tolerance_ok(y, ref.epilogue(acc_ref, s_a, qw["s1"])).all()
 
 
 def test_gemm_zero_token_and_strided_output():
