@@ -10,7 +10,7 @@ from the 256 MB Infinity Cache or the L2.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
-Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
 from __future__ import annotations
 
@@ -216,7 +216,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this W4A8 GEMM build has no multi-GPU path "
+        print("bench.py measures one GPU only: this W4A8 GEMM library has no multi-GPU path "
               "(the layer would shard by output columns or by K with an int32 all-reduce; "
               "neither is built).", file=sys.stderr)
         sys.exit(2)
