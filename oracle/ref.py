@@ -33,7 +33,7 @@ Every rounding is pinned: fp32 operations are single IEEE operations
 round-to-nearest-even, rint is round-half-to-even.  Integer divisions that
 the definition states as exact rationals are done in integers.
 
-Parity pins for every function live in tests/test_oracle_*.py.
+Parity pins for every function live in tests/test_oracle_pins.py.
 """
 from __future__ import annotations
 
@@ -262,13 +262,6 @@ def gemm_acc(a8: np.ndarray, w8hat: np.ndarray) -> np.ndarray:
     if out.size and np.abs(out).max() >= 2 ** 31:
         raise OverflowError("accumulator leaves int32")
     return out
-
-
-def gemm_acc_entries(a8: np.ndarray, w8hat_rows: np.ndarray, rows, cols_local):
-    """O4 for a list of (m, n) pairs; w8hat_rows holds the needed rows of W8^."""
-    a = np.asarray(a8, dtype=np.int64)
-    w = np.asarray(w8hat_rows, dtype=np.int64)
-    return np.einsum("ik,ik->i", a[rows], w[cols_local])
 
 
 # ---------------------------------------------------------------- O5

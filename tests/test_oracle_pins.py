@@ -84,13 +84,15 @@ def test_to_f16_matches_exact_rational_rounding():
 
 
 # ------------------------------------------------------------ O2 level 2
-def level2_domain_check(level2, limit=119):
+def level2_domain_check(level2, limit=119, decode=ref.decode):
     """Exhaustive over every (lo, hi, w8) with -limit <= lo <= 0 <= hi <= limit.
 
     A level-2 result for one element depends only on its group's lo, hi and
     on its own value, so groups [lo, hi, lo..hi] cover the whole domain.
     Returns the number of violations of: s2 in [1,16], z in [0,15],
     q in [0,15], decode in int8, and |w8 - decode| <= s2/2 (where unclamped).
+    The decoded values come from `decode` (the oracle's own by default), with
+    each group as one row of one group.
     """
     width = 2 * limit + 3
     los, his = np.meshgrid(np.arange(-limit, 1), np.arange(0, limit + 1), indexing="ij")
@@ -104,7 +106,7 @@ def level2_domain_check(level2, limit=119):
     s2 = s2.astype(np.int64)
     z = z.astype(np.int64)
     q = q.astype(np.int64)
-    dec = (q - z[:, None]) * s2[:, None]
+    dec = np.asarray(decode(q, z[:, None], s2[:, None], groups.shape[1]), dtype=np.int64)
     bad = 0
     bad += int(np.sum((s2 < 1) | (s2 > 16)))
     bad += int(np.sum((z < 0) | (z > 15)))
@@ -151,6 +153,125 @@ def test_level2_identity_special_case():
     g[:, 0] = 15
     s2, z, q = ref.level2_groups(g)
     assert (s2 == 1).all() and (z == 0).all() and (q == g).all()
+
+
+# ------------------------------------------------------------ decode
+def decode_golden_cases():
+    """Parse decode_cases.txt into [(name, g, q, z, s2, [(n, k, q, want)])]."""
+    cases = []
+    for line in read_rows("decode_cases.txt"):
+        tok = line.split()
+        if tok[0] == "case":
+            g, k, n = int(tok[2]), int(tok[3]), int(tok[4])
+            groups = k // g
+            rows = np.arange(n)[:, None]
+            cols = np.arange(k)[None, :]
+            q = ((5 * cols + 3 * rows) % 16).astype(np.uint8)
+            z = np.full((n, groups), 255, dtype=np.uint8)     # every row is listed
+            s2 = np.zeros((n, groups), dtype=np.uint8)
+            cases.append([tok[1], g, q, z, s2, []])
+        elif tok[0] == "zs":
+            r = int(tok[1])
+            zs, s2s = " ".join(tok[2:]).split("|")
+            cases[-1][3][r] = [int(t) for t in zs.split()]
+            cases[-1][4][r] = [int(t) for t in s2s.split()]
+        else:
+            cases[-1][5].append(tuple(int(t) for t in tok))
+    return cases
+
+
+def decode_golden_check(decode):
+    """Mismatches of decode(q, z, s2, g) against the hand-worked values."""
+    bad = []
+    for name, g, q, z, s2, points in decode_golden_cases():
+        assert (z != 255).all(), name
+        dec = np.asarray(decode(q, z, s2, g))
+        assert dec.shape == q.shape, name
+        for n, k, q_w, want in points:
+            if int(q[n, k]) != q_w or int(dec[n, k]) != want:
+                bad.append((name, n, k, int(q[n, k]), int(dec[n, k]), want))
+    return bad
+
+
+def test_decode_golden():
+    assert decode_golden_check(ref.decode) == []
+
+
+def dequant_loop_check(decode, gs=(32, 64, 128, 0)):
+    """Plain Python loops over the logical arrays alone, element by element:
+    W^[n][k] = s1[n] * (q[n][k] - z[n][k // g]) * s2[n][k // g], then the
+    dequant-then-matmul Y[m][n] = sum_k (s_a[m] * A8[m][k]) * W^[n][k] in
+    exact rationals; `decode` must give the same integers and s_a * s1 *
+    (A8 @ decode^T) the same Y.  g = 0 is per-channel (one group per row).
+    Returns the number of mismatching values."""
+    bad = 0
+    n, k, m = 6, 256, 3
+    w = synth.weights(n, k, seed=41, dist="student_t4")
+    a = synth.activations(m, k, seed=42)
+    a8, s_a = ref.quant_act(a)
+    for g in gs:
+        qw = ref.quantize_weights(w, g)
+        q, z, s2, s1 = qw["q"], qw["z"], qw["s2"], qw["s1"]
+        geff = k if g == 0 else g
+        dec = np.asarray(decode(q, z, s2, geff))
+        wq = [[Fraction(float(s1[i])) * (int(q[i, t]) - int(z[i, t // geff])) * int(s2[i, t // geff])
+               for t in range(k)] for i in range(n)]
+        for i in range(n):
+            for t in range(k):
+                if Fraction(float(s1[i])) * int(dec[i, t]) != wq[i][t]:
+                    bad += 1
+        acc = a8.astype(np.int64) @ dec.astype(np.int64).T
+        for r in range(m):
+            sa = Fraction(float(s_a[r]))
+            for i in range(n):
+                y = sum(sa * int(a8[r, t]) * wq[i][t] for t in range(k))
+                if y != sa * Fraction(float(s1[i])) * int(acc[r, i]):
+                    bad += 1
+    return bad
+
+
+def test_dequant_loop_matches_decode():
+    assert dequant_loop_check(ref.decode) == 0
+
+
+def test_decoded_weights_is_decode_of_the_packed_arrays():
+    w = synth.weights(8, 256, seed=43)
+    for g in (32, 64, 128, 0):
+        qw = ref.quantize_weights(w, g)
+        geff = 256 if g == 0 else g
+        assert qw["g_eff"] == geff
+        assert np.array_equal(ref.decoded_weights(qw), ref.decode(qw["q"], qw["z"], qw["s2"], geff))
+
+
+def _dec_mod_group(q, z, s2, g):               # group index k % G instead of k // g
+    k = q.shape[1]
+    j = np.arange(k) % z.shape[1]
+    return (q.astype(np.int32) - z[:, j].astype(np.int32)) * s2[:, j].astype(np.int32)
+
+
+def _dec_plus_s2(q, z, s2, g):                 # an extra +s2 offset
+    return ref.decode(q, z, s2, g) + np.repeat(s2.astype(np.int32), g, axis=1)
+
+
+def _dec_neighbour_z(q, z, s2, g):             # z taken from the next group
+    zz = np.roll(z, -1, axis=1) if z.shape[1] > 1 else z.astype(np.int32) + 1
+    return ref.decode(q, zz, s2, g)
+
+
+def _dec_unscaled_z(q, z, s2, g):              # q * s2 - z: the zero not scaled
+    zz = np.repeat(z.astype(np.int32), g, axis=1)
+    ss = np.repeat(s2.astype(np.int32), g, axis=1)
+    return q.astype(np.int32) * ss - zz
+
+
+@pytest.mark.parametrize("mutant", [_dec_mod_group, _dec_plus_s2, _dec_neighbour_z,
+                                    _dec_unscaled_z])
+def test_decode_pins_catch_mutants(mutant):
+    # each plausible decode mistake fails the element-wise pins, not only the
+    # whole-layer norm bound
+    assert decode_golden_check(mutant) != []
+    assert dequant_loop_check(mutant, gs=(32, 0)) > 0
+    assert level2_domain_check(ref.level2_groups, decode=mutant) > 0 or mutant is _dec_mod_group
 
 
 # ------------------------------------------------------------ O1 level 1
