@@ -4,6 +4,7 @@ import ctypes
 import subprocess
 
 import numpy as np
+import torch
 import pytest
 
 import synth
@@ -312,6 +313,35 @@ def test_linear_validates_before_any_hip_call():
     assert call(opts=ctypes.byref(opts)) == 1          # negative workgroup count
     opts = w4.GemmOpts(3)
     assert call(m=4, k=131072, lda=131072, lda8=131072, opts=ctypes.byref(opts)) == 2  # long K
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0,
+                    reason="passes fake device pointers: host-only check")
+def test_linear_checks_the_gemm_before_the_quantizer():
+    """w4a8_linear on the two-launch path rejects what w4a8_gemm would reject
+    before it enqueues the quantizer: the fake pointers are never used."""
+    L = w4.lib
+    fake = ctypes.c_void_p(4096)
+    m, n, k, g = 100, 4096, 14336, 128
+    assert L.w4a8_linear_launches(m, n, k, g, None) == 3           # K split: needs a workspace
+    need = L.w4a8_gemm_workspace_size(m, n, k, g, None)
+    assert need > 0
+    # (a, lda, m, k, blob, n, g, y, ldy, a8, lda8, s_a, acc, ldacc, ws, ws_bytes, opts, stream)
+    assert L.w4a8_linear(fake, k, m, k, fake, n, g, fake, n, fake, k, fake, None, 0, None, 0,
+                         None, None) == 3                           # no workspace
+    assert L.w4a8_linear(fake, k, m, k, fake, n, g, fake, n, fake, k, fake, None, 0, fake,
+                         need - 16, None, None) == 3                # workspace too small
+    assert L.w4a8_linear(fake, k, m, k, fake, n, g, fake, n, fake, k, fake, None, 0,
+                         ctypes.c_void_p(4104), need, None, None) == 1   # misaligned workspace
+    opts = w4.GemmOpts(1)
+    assert L.w4a8_linear(fake, k, m, k, fake, n, g, fake, n, fake, k, fake, None, 0, None, 0,
+                         ctypes.byref(opts), None) == 2             # skinny: at most 64 rows
+    opts = w4.GemmOpts(2, 0, 0, 0, 0, 0, 17)
+    assert L.w4a8_linear(fake, k, m, k, fake, n, g, fake, n, fake, k, fake, None, 0, None, 0,
+                         ctypes.byref(opts), None) == 1             # more slices than allowed
+    opts = w4.GemmOpts(2, 0, 0, 7)
+    assert L.w4a8_linear(fake, k, m, k, fake, n, g, fake, n, fake, k, fake, None, 0, None, 0,
+                         ctypes.byref(opts), None) == 1             # no such row-tile count
 
 
 def test_linear_launch_plan():

@@ -219,6 +219,28 @@ extern "C" size_t w4a8_gemm_workspace_size(int m, int n, int k, int g,
   return pl.status == W4A8_OK ? pl.workspace : 0;
 }
 
+namespace {
+
+// Every host-side check of a w4a8_gemm call, with no HIP call: shape, the
+// plan (automatic or forced) and the workspace.  w4a8_linear runs it before
+// it launches the quantizer, so a call the GEMM would reject leaves no
+// kernel behind.  m > 0; a8/s_a may be checked by the caller instead (the
+// fused layer writes them).
+w4a8_status check_gemm(const Plan& pl, int k, int g, void* workspace_dev, size_t workspace_bytes) {
+  if (pl.status != W4A8_OK) return pl.status;
+  const int gpb = groups_per_block(k, g);
+  if (pl.variant == 1 && !skinny_config_supported(pl.skinny, k, gpb))
+    return W4A8_ERR_INVALID_ARGUMENT;
+  if (pl.variant == 2 && !tiled_config_supported(pl.tiled)) return W4A8_ERR_INVALID_ARGUMENT;
+  if (pl.workspace) {
+    if (!workspace_dev || workspace_bytes < pl.workspace) return W4A8_ERR_BUFFER_TOO_SMALL;
+    if (!aligned16(workspace_dev)) return W4A8_ERR_INVALID_ARGUMENT;
+  }
+  return W4A8_OK;
+}
+
+}  // namespace
+
 extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev, int m,
                                  const void* blob_dev, int n, int k, int g, uint16_t* y_dev,
                                  int ldy, int32_t* acc_dev, int ldacc, void* workspace_dev,
@@ -232,15 +254,9 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
   if (!aligned16(a8_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
 
   const Plan pl = plan_gemm(m, n, k, opts);
-  if (pl.status != W4A8_OK) return pl.status;
+  const w4a8_status st = check_gemm(pl, k, g, workspace_dev, workspace_bytes);
+  if (st != W4A8_OK) return st;
   const int gpb = groups_per_block(k, g);
-  if (pl.variant == 1 && !skinny_config_supported(pl.skinny, k, gpb))
-    return W4A8_ERR_INVALID_ARGUMENT;
-  if (pl.variant == 2 && !tiled_config_supported(pl.tiled)) return W4A8_ERR_INVALID_ARGUMENT;
-  if (pl.workspace) {
-    if (!workspace_dev || workspace_bytes < pl.workspace) return W4A8_ERR_BUFFER_TOO_SMALL;
-    if (!aligned16(workspace_dev)) return W4A8_ERR_INVALID_ARGUMENT;
-  }
 
   Sections sec = sections(n, k, g);
   const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
@@ -357,8 +373,11 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
     p.s_a_out = s_a_dev;
     return device_status(launch_gemm_fused(p, a_dev, lda, groups_per_block(k, g), fc, s));
   }
-  // two launches: the quantizer, then the GEMM on its output
-  w4a8_status st = w4a8_quant_act(a_dev, m, k, lda, a8_dev, lda8, s_a_dev, stream);
+  // two launches: the quantizer, then the GEMM on its output; the GEMM's
+  // checks run first, so that a call it would reject enqueues nothing
+  w4a8_status st = check_gemm(plan_gemm(m, n, k, opts), k, g, workspace_dev, workspace_bytes);
+  if (st != W4A8_OK) return st;
+  st = w4a8_quant_act(a_dev, m, k, lda, a8_dev, lda8, s_a_dev, stream);
   if (st != W4A8_OK) return st;
   return w4a8_gemm(a8_dev, lda8, s_a_dev, m, blob_dev, n, k, g, y_dev, ldy, acc_dev, ldacc,
                    workspace_dev, workspace_bytes, opts, stream);

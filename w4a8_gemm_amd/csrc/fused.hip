@@ -256,6 +256,10 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
   // MF are corrected: with MF <= 4 the valid rows are values 0 .. MF-1 of
   // lanes 0 .. 15, and the rest are never stored.
   constexpr bool FACTORED = GPB == 0 || GPB == 1 || GPB == 2;
+  // add_group's 24-bit products are exact while a factored group spans at
+  // most 2048 k: |sum a| <= 127 * 2048 and |sum a * q|, |z * sum a| <=
+  // 127 * 15 * 2048, so every factor and difference stays below 2^23
+  static_assert(!FACTORED || KBW * 128 <= 2048, "factored groups need wave ranges of <= 2048 k");
   constexpr int NV = MF < 4 ? MF : 4;
   const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
   auto codes = [&](const u32x4& qc, int h) { return h ? codes16(qc.z, qc.w) : codes16(qc.x, qc.y); };
