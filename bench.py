@@ -3,12 +3,19 @@
 One step = one pass of the whole hot path over a workload: for every run
 (M, layer) of the workload, the per-token activation quantizer and the W4A8
 GEMM through the C ABI library (one fused launch, w4a8_linear, where M is
-small enough; else w4a8_quant_act then w4a8_gemm).  Inputs are resident in HBM
-when the timed region starts.  Weight blobs rotate through a pool of copies
-of at least 1 GiB so that every GEMM reads its weights from HBM rather than
-from the 256 MB Infinity Cache or the L2.
+small enough; else w4a8_quant_act then w4a8_gemm).  The default workload
+spans the metric's whole range in one step: the Llama-3-8B layers at
+M = 1, 4, 16 (decode) and 64, 256, 1024 (batched serving) and the
+Qwen1.5-72B layers at M = 2048, 4096.  Inputs are resident in HBM when the
+timed region starts.
+
+Weight blobs rotate through copies, at least 512 MiB of them per layer, and
+every use of a layer takes its next copy, so that no launch finds its weights
+in the 256 MB Infinity Cache or an L2 (a layer's copy comes back only after
+at least 512 MiB of that layer's other copies have been read).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --stream-probe          # read-only HBM stream ceiling
 
 Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
@@ -17,7 +24,9 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
+import platform
 import sys
 import time
 
@@ -29,18 +38,26 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS (2.4 GHz)
+METRIC = "W4A8 GEMM TOPS + HBM GB/s vs roofline at M=1..4096 (Llama-3-8B layer shapes)"
 # HBM counters are keyed to the sources of the kernel they were taken on
 CSRC = os.path.join(ROOT, "w4a8_gemm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
-
 CODEBOOK_NF = 1   # g value of the non-uniform codebook mode (no meta)
 
 # sources of the kernels each counter entry covers (small M: fused and
-# skinny; large M: tiled with its K-split reduction)
+# skinny; larger M: tiled with its K-split reduction)
 SKINNY_SOURCES = ["fused.hip", "skinny.hip", "gemm_common.h", "quant_common.h", "codebook.h"]
 TILED_SOURCES = ["tiled.hip", "gemm_common.h", "quant_common.h", "codebook.h"]
+
+# launch groups whose mean duration is timed on its own: the two graded
+# regimes (M <= 16, HBM-bound; M >= 1024, MFMA-bound) and the transition
+GROUPS = {
+    "m_le_16": (lambda m: m <= 16, "hbm", SKINNY_SOURCES),
+    "m_17_1023": (lambda m: 16 < m < 1024, None, TILED_SOURCES),
+    "m_ge_1024": (lambda m: m >= 1024, "mfma", TILED_SOURCES),
+}
 
 
 def meta_bytes(n, k, g):
@@ -77,25 +94,38 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """Mean HBM bytes per GEMM launch on `workload` from committed rocprofv3
-    counter runs, if they were taken on the current kernel sources; else None."""
+def load_traffic(workload, group):
+    """Mean HBM bytes per launch of `group` on `workload` from committed
+    rocprofv3 counter runs, if they were taken on the current kernel sources;
+    else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             entries = json.load(f)["entries"]
     except (OSError, ValueError, KeyError):
         return None
     for t in entries:
-        if t.get("workload") == workload and t.get("source_sha256_16") == source_hash(t["sources"]):
+        if (t.get("workload") == workload and t.get("group") == group
+                and t.get("source_sha256_16") == source_hash(t["sources"])):
             return t.get("bytes_per_launch")
     return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 class HipEvent:
     """A HIP event created with hipEventDisableSystemFence, recorded on a given
     stream.  Timing-only events without the system-scope cache writeback and
     invalidate that a default event performs, so the interval between two of
-    them is closer to the kernel in between.  Uses the HIP runtime torch has
+    them is closer to the kernels in between.  Uses the HIP runtime torch has
     already loaded (same process-wide runtime as the library)."""
     _lib = None
     DISABLE_SYSTEM_FENCE = 0x20000000
@@ -135,65 +165,134 @@ class HipEvent:
         return ms.value
 
 
-def cpu_baseline(runs, weights, unit, budget_s=15.0):
+def gpu_spin(seconds):
+    """Keep the GPU busy while the host enqueues the region behind it."""
+    import torch
+    torch.cuda._sleep(int(2.4e9 * seconds))
+
+
+CPU_ROWS, CPU_COLS = 128, 256   # the oracle's sample of each run
+
+
+def cpu_baseline(runs, weights, acts, unit, budget_s=15.0, rows_max=CPU_ROWS, cols_max=CPU_COLS):
     """The oracle, untuned, on a bounded sample of the same workload: every
-    run, restricted to the first `cols` output columns of each layer.  The
-    rate is in the metric's unit (GB/s of algorithmic bytes, or TOPS); the
-    time of each oracle stage is reported beside it."""
+    run restricted to its first `rows_max` tokens and its first `cols_max`
+    output columns (all of K); `weights` and `acts` hold those rows of W
+    and A.  The rate is in the metric's unit (GB/s of algorithmic bytes, or
+    TOPS); the time of each oracle stage is reported beside it."""
     from oracle import ref
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    cols = 2048
-    qws = {}
-    for (layer, n, k, g), w in weights.items():
-        qws[layer] = ref.quantize_weights(w[:cols], g)      # offline pack: not timed
-    acts = {}
-    for (m, layer, n, k, g, seed) in runs:
-        acts[(m, layer)] = synth.activations(m, k, seed=seed)
+    qws = {key: ref.quantize_weights(w[:cols_max], key[2]) for key, w in weights.items()}
     done_bytes = done_ops = 0.0
     stage = {"quant_act": 0.0, "decode_and_gemm": 0.0, "epilogue": 0.0}
     t0 = time.perf_counter()
     passes = 0
     while True:
-        for (m, layer, n, k, g, seed) in runs:
-            a = acts[(m, layer)]
+        for (m, layer, n, k, g, seed, key) in runs:
+            a = acts[(m, key)][:rows_max]
+            qw = qws[key]
             t1 = time.perf_counter()
             a8, s_a = ref.quant_act(a)
             t2 = time.perf_counter()
-            w8hat = ref.decoded_weights(qws[layer])
-            acc = ref.gemm_acc(a8, w8hat)
+            acc = ref.gemm_acc(a8, ref.decoded_weights(qw))
             t3 = time.perf_counter()
-            ref.epilogue(acc, s_a, qws[layer]["s1"])
+            ref.epilogue(acc, s_a, qw["s1"])
             t4 = time.perf_counter()
             stage["quant_act"] += t2 - t1
             stage["decode_and_gemm"] += t3 - t2
             stage["epilogue"] += t4 - t3
-            ncols = min(cols, n)
-            done_bytes += algo_bytes(m, ncols, k, g) + quant_bytes(m, k)
-            done_ops += 2.0 * m * ncols * k
+            rows, cols = a.shape[0], min(cols_max, n)
+            done_bytes += algo_bytes(rows, cols, k, g) + quant_bytes(rows, k)
+            done_ops += 2.0 * rows * cols * k
         passes += 1
-        if time.perf_counter() - t0 >= budget_s or passes >= 200:
+        if time.perf_counter() - t0 >= budget_s or passes >= 500:
             break
     dt = time.perf_counter() - t0
     value = done_ops / dt / 1e12 if unit == "TOPS" else done_bytes / dt / 1e9
-    return {"value": round(value, 4), "unit": unit, "cores": int(cores),
+    return {"value": round(value, 6), "unit": unit, "cores": int(cores),
             "kind": "oracle",
-            "sample": f"every run of the workload restricted to the first {cols} output "
-                      f"columns of each layer, {passes} pass(es), {dt:.1f} s",
+            "sample": f"every run of the workload restricted to its first {rows_max} tokens and "
+                      f"first {cols_max} output columns (all of K), {passes} pass(es), "
+                      f"{dt:.1f} s",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "stage_seconds": {key: round(v, 3) for key, v in stage.items()}}
 
 
+# ------------------------------------------------------------------ stream probe
+def stream_probe(args):
+    """Read-only stream kernel (w4a8_read_probe) over the decode layers' sizes
+    and beyond: per size, the best grid's mean launch time, each launch
+    reading a region of a 2 GiB buffer that no launch of the last 2 GiB read."""
+    import torch
+    import w4a8_gemm_amd as w4
+    dev = torch.device("cuda:0")
+    span = 2 << 30
+    buf = torch.empty(span, dtype=torch.uint8, device=dev)
+    buf.random_(0, 256)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    stream_ptr = int(torch.cuda.current_stream().cuda_stream)
+    # decimal MB: the Llama-3-8B decode layers' algorithmic bytes at M = 1
+    # (O 8.6, QKV 12.9, down 30.1, gate+up 60.2), then larger
+    sizes_mb = [4.0, 8.6, 12.9, 30.1, 60.2, 128.0, 512.0]
+    grids = [256, 512, 1024, 2048, 4096, 8192]
+    out = []
+    for mb in sizes_mb:
+        nbytes = int(mb * 1e6) // 4096 * 4096
+        slots = span // nbytes
+        reps = int(max(20, min(200, slots)))
+        best = None
+        per_grid = {}
+        for wgs in grids:
+            offsets = [(i % slots) * nbytes for i in range(reps)]
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for off in offsets:
+                    w4.read_probe(buf, off, nbytes, wgs, sink)
+            gr.replay()
+            torch.cuda.synchronize()
+            h0, h1 = HipEvent(), HipEvent()
+            gpu_spin(0.01)
+            h0.record(stream_ptr)
+            gr.replay()
+            h1.record(stream_ptr)
+            torch.cuda.synchronize()
+            us = h0.elapsed_time(h1) * 1e3 / reps
+            per_grid[wgs] = round(us, 3)
+            if best is None or us < best[0]:
+                best = (us, wgs)
+            del gr
+        us, wgs = best
+        out.append({"mb": round(nbytes / 1e6, 3), "us": round(us, 3),
+                    "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_8tbs": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "best_workgroups": wgs, "us_by_workgroups": per_grid})
+        log(f"read probe {nbytes / 1e6:8.1f} MB: {us:8.2f} us  "
+            f"{nbytes / (us * 1e-6) / 1e9:7.1f} GB/s  ({wgs} workgroups)")
+    # t = t0 + bytes / bw, least squares over the sizes
+    x = np.array([o["mb"] * 1e6 for o in out])
+    y = np.array([o["us"] * 1e-6 for o in out])
+    slope, t0 = np.polyfit(x, y, 1)
+    print(json.dumps({"probe": "read-only HBM stream (w4a8_read_probe), graph replays, "
+                               "HIP events around each graph",
+                      "sizes": out,
+                      "fit": {"t0_us": round(t0 * 1e6, 3), "bw_gbps": round(1 / slope / 1e9, 1)}}),
+          flush=True)
+
+
+# ------------------------------------------------------------------ the layer
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_8b_decode",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="m1_to_4096",
                     choices=[k for k in synth.workloads() if k != "tiny"] + ["tiny"])
-    ap.add_argument("--rotation-gib", type=float, default=1.0)
+    ap.add_argument("--rotation-mib", type=float, default=512.0,
+                    help="weight copies per layer: at least this many MiB of them")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--runs-json", default="")
     ap.add_argument("--no-graph", action="store_true",
@@ -207,6 +306,8 @@ def main():
     ap.add_argument("--codebook", action="store_true",
                     help="pack every layer in the non-uniform codebook mode (register "
                          "table decode) instead of the workload's group size")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="time the read-only HBM stream probe instead of the layer")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
@@ -217,9 +318,12 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this W4A8 GEMM library has no multi-GPU path "
-              "(the layer would shard by output columns or by K with an int32 all-reduce; "
+              "(the layer would shard by output columns, or by K with an int32 all-reduce; "
               "neither is built).", file=sys.stderr)
         sys.exit(2)
+    if args.stream_probe:
+        stream_probe(args)
+        return
 
     import torch
     import w4a8_gemm_amd as w4
@@ -227,39 +331,56 @@ def main():
 
     wl_names = list(synth.workloads().keys())
     items = synth.workloads()[args.workload]
-    cfg_idx = wl_names.index(args.workload)
     if args.codebook:
         items = [(c, m, layer, n, k, CODEBOOK_NF, dist) for (c, m, layer, n, k, g, dist) in items]
+    if args.w4a16 and max(it[1] for it in items) > 64:
+        print("--w4a16: the W4A16 comparison kernel covers M <= 64 only", file=sys.stderr)
+        sys.exit(2)
 
-    # weights: one per (layer, g); seeds as the parity tests use them
-    layer_keys = []
-    for (_, m, layer, n, k, g, dist) in items:
-        key = (layer, n, k, g, dist)
-        if key not in layer_keys:
-            layer_keys.append(key)
-    weights, blobs = {}, {}
-    for shape_idx, (layer, n, k, g, dist) in enumerate(layer_keys):
-        log(f"packing {layer} n={n} k={k} g={g}")
-        w = synth.weights(n, k, seed=synth.weight_seed(cfg_idx, shape_idx, 0), dist=dist)
-        blobs[(layer, g)] = w4.to_device(w4.pack(w, g), dev)
+    # layers: one weight matrix per (N, K, g, dist); seeds as the parity
+    # tests draw them, from the workload each run comes from
+    layer_of, seeds = {}, {}
+    shape_lists = {}
+    for (cfg, m, layer, n, k, g, dist) in items:
+        key = (n, k, g, dist)
+        shapes = shape_lists.setdefault(cfg, [])
+        if key not in shapes:
+            shapes.append(key)
+        if key not in layer_of:
+            layer_of[key] = layer
+            seeds[key] = synth.weight_seed(wl_names.index(cfg), shapes.index(key), 0)
+    copies, weights = {}, {}
+    rot_bytes = args.rotation_mib * 2 ** 20
+    for key in layer_of:
+        n, k, g, dist = key
+        log(f"packing {layer_of[key]} n={n} k={k} g={g}")
+        w = synth.weights(n, k, seed=seeds[key], dist=dist)
+        blob = w4.to_device(w4.pack(w, g), dev)
+        ncopy = max(2, math.ceil(rot_bytes / blob.numel()))
+        copies[key] = [blob] + [blob.clone() for _ in range(ncopy - 1)]
         if not args.no_cpu_baseline:
-            weights[(layer, n, k, g)] = w[:2048].copy()
+            weights[key] = w[:CPU_COLS].copy()
         del w
-    per_copy = sum(b.numel() for b in blobs.values())
-    ncopies = max(2, int(np.ceil(args.rotation_gib * 2 ** 30 / per_copy)))
-    pool = [blobs] + [{key: b.clone() for key, b in blobs.items()} for _ in range(ncopies - 1)]
-    log(f"rotation pool: {ncopies} copies x {per_copy / 2**20:.1f} MiB")
+    pool_bytes = sum(len(c) * c[0].numel() for c in copies.values())
+    log(f"rotation pool: {pool_bytes / 2**30:.2f} GiB, "
+        + ", ".join(f"{layer_of[key]} {len(c)}" for key, c in copies.items()))
 
-    runs = []   # (m, layer, n, k, g, seed)
+    runs = []   # (m, layer, n, k, g, seed, key)
     m_index = {}
-    for (_, m, layer, n, k, g, dist) in items:
-        shape_idx = layer_keys.index((layer, n, k, g, dist))
-        mi = m_index.setdefault((layer, g), {}).setdefault(m, len(m_index[(layer, g)]))
-        runs.append((m, layer, n, k, g, synth.act_seed(cfg_idx, shape_idx, mi)))
+    for (cfg, m, layer, n, k, g, dist) in items:
+        key = (n, k, g, dist)
+        shape_idx = shape_lists[cfg].index(key)
+        mi = m_index.setdefault((cfg, key), {}).setdefault(m, len(m_index[(cfg, key)]))
+        runs.append((m, layer, n, k, g, synth.act_seed(wl_names.index(cfg), shape_idx, mi), key))
+    nr = len(runs)
 
-    bufs = []
-    for (m, layer, n, k, g, seed) in runs:
-        a = torch.from_numpy(synth.activations(m, k, seed=seed)).to(dev)
+    bufs, acts_host = [], {}
+    for (m, layer, n, k, g, seed, key) in runs:
+        a_np = synth.activations(m, k, seed=seed)
+        if not args.no_cpu_baseline:
+            acts_host[(m, key)] = a_np[:CPU_ROWS].copy()
+        a = torch.from_numpy(a_np).to(dev)
+        del a_np
         a8 = torch.empty((m, k), dtype=torch.int8, device=dev)
         s_a = torch.empty((m,), dtype=torch.float16, device=dev)
         y = torch.empty((m, n), dtype=torch.float16, device=dev)
@@ -267,25 +388,34 @@ def main():
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
         bufs.append((a, a8, s_a, y, ws))
 
-    nr = len(runs)
-
     stream_ptr = int(torch.cuda.current_stream().cuda_stream)
 
     # small M: quantization fused into the GEMM (one launch, w4a8_linear);
-    # else the quantizer, then the GEMM; events bracket the GEMM launch
+    # else the quantizer, then the GEMM
     fused = [int(w4.lib.w4a8_linear_launches(m, n, k, g, None)) == 1
-             and args.static_scale is None and not args.w4a16 for (m, _, n, k, g, _) in runs]
-    if args.w4a16 and max(r[0] for r in runs) > 64:
-        print("--w4a16: the W4A16 comparison kernel covers M <= 64 only", file=sys.stderr)
-        sys.exit(2)
+             and args.static_scale is None and not args.w4a16
+             for (m, _, n, k, g, _, _) in runs]
 
-    def launch_step(copy, record=None, gemm_only=False):
-        for r, (m, layer, n, k, g, _) in enumerate(runs):
+    # every use of a layer takes its next copy
+    counter = {key: 0 for key in copies}
+
+    def next_copies(sel):
+        out = {}
+        for r in sel:
+            key = runs[r][6]
+            out[r] = copies[key][counter[key] % len(copies[key])]
+            counter[key] += 1
+        return out
+
+    def launch_step(blobs, sel, record=None, gemm_only=False):
+        for r in sel:
+            m, layer, n, k, g, _, _ = runs[r]
             a, a8, s_a, y, ws = bufs[r]
+            blob = blobs[r]
             if args.w4a16:
                 if record is not None:
                     record[r][0].record(stream_ptr)
-                w4.w4a16(a, copy[(layer, g)], n, k, g, y=y)
+                w4.w4a16(a, blob, n, k, g, y=y)
                 if record is not None:
                     record[r][1].record(stream_ptr)
                 continue
@@ -298,30 +428,31 @@ def main():
             if record is not None:
                 record[r][0].record(stream_ptr)
             if fused[r]:
-                w4.linear(a, copy[(layer, g)], n, k, g, y=y, a8=a8, s_a=s_a, workspace=ws)
+                w4.linear(a, blob, n, k, g, y=y, a8=a8, s_a=s_a, workspace=ws)
             else:
-                w4.gemm(a8, s_a, copy[(layer, g)], n, k, g, y=y, workspace=ws)
+                w4.gemm(a8, s_a, blob, n, k, g, y=y, workspace=ws)
             if record is not None:
                 record[r][1].record(stream_ptr)
 
-    def new_events():
-        return [(HipEvent(), HipEvent()) for _ in range(nr)]
+    all_runs = list(range(nr))
+    step_ops = sum(2.0 * m * n * k for (m, _, n, k, g, _, _) in runs)
+    spin_s = max(0.02, 2e-5 * args.steps * nr)
 
-    # Pass 1 (per-launch durations for the roofline): `steps` eager steps
-    # enqueued from the host behind a GPU spin kernel, so that the whole
-    # region is queued when the GPU reaches it; events recorded on the launch
-    # stream around each GEMM launch give its on-GPU duration.
-    events = [new_events() for _ in range(args.steps)]
+    # Pass 1 (per-launch table): `steps` eager steps enqueued from the host
+    # behind a GPU spin kernel, so that the whole region is queued when the
+    # GPU reaches it; events on the launch stream around each GEMM launch
+    # give its duration (dispatch included).
     for i in range(args.warmup):
-        launch_step(pool[i % ncopies])
+        launch_step(next_copies(all_runs), all_runs)
     torch.cuda.synchronize()
+    events = [[(HipEvent(), HipEvent()) for _ in range(nr)] for _ in range(args.steps)]
+    plans = [next_copies(all_runs) for _ in range(args.steps)]
     t_start, t_end = HipEvent(), HipEvent()
-    spin_s = max(0.02, 5e-5 * args.steps * nr)
-    torch.cuda._sleep(int(2.4e9 * spin_s))          # GPU spin while the host enqueues
+    gpu_spin(spin_s)
     t_start.record(stream_ptr)
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        launch_step(pool[i % ncopies], record=events[i])
+        launch_step(plans[i], all_runs, record=events[i])
     t_end.record(stream_ptr)
     enqueue_s = time.perf_counter() - wall0
     torch.cuda.synchronize()
@@ -329,86 +460,77 @@ def main():
     ms_per_step_eager = total_ms / args.steps
     per_step_gemm = [[events[i][r][0].elapsed_time(events[i][r][1]) for r in range(nr)]
                      for i in range(args.steps)]
+    del plans
     log(f"eager pass: host enqueue {enqueue_s * 1e3:.1f} ms, GPU spin ~{spin_s * 1e3:.0f} ms, "
         f"timed GPU region {total_ms:.2f} ms")
-    if enqueue_s * 1e3 > total_ms + 1e3 * spin_s:
-        log("warning: the host enqueue outlasted the GPU spin; the GPU may have idled")
 
-    # Pass 2 (the timed steps): each step captured once as a HIP graph (one
-    # graph per weight copy of the rotation pool) and replayed, as a serving
-    # loop runs its decode steps; `steps` replays are timed between two
-    # synchronizations, enqueued behind a GPU spin.
+    def graph_pass(sel, gemm_only):
+        """Capture warmup + steps graphs of the runs `sel` (each with the next
+        weight copies), replay the warmup ones, then time `steps` replays
+        between two HIP events on the launch stream; returns ms per graph."""
+        graphs = []
+        for _ in range(args.warmup + args.steps):
+            gr = torch.cuda.CUDAGraph()
+            blobs = next_copies(sel)
+            with torch.cuda.graph(gr):
+                launch_step(blobs, sel, gemm_only=gemm_only)
+            graphs.append(gr)
+        for gr in graphs[:args.warmup]:
+            gr.replay()
+        torch.cuda.synchronize()
+        h0, h1 = HipEvent(), HipEvent()
+        gpu_spin(spin_s)
+        h0.record(stream_ptr)
+        for gr in graphs[args.warmup:]:
+            gr.replay()
+        h1.record(stream_ptr)
+        torch.cuda.synchronize()
+        return h0.elapsed_time(h1) / args.steps
+
+    # Pass 2 (the timed steps): each step captured as a HIP graph and
+    # replayed, as a serving loop issues its steps.
     ms_per_step, timing = ms_per_step_eager, "eager launches"
     if not args.no_graph:
         try:
-            graphs = []
-            for i in range(ncopies):
-                gr = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gr):
-                    launch_step(pool[i])
-                graphs.append(gr)
-            for i in range(args.warmup):
-                graphs[i % ncopies].replay()
-            torch.cuda.synchronize()
-            g0 = torch.cuda.Event(enable_timing=True)
-            g1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(int(2.4e9 * spin_s))
-            g0.record()
-            for i in range(args.steps):
-                graphs[i % ncopies].replay()
-            g1.record()
-            torch.cuda.synchronize()
-            ms_per_step = g0.elapsed_time(g1) / args.steps
+            ms_per_step = graph_pass(all_runs, gemm_only=False)
             timing = "HIP graph replay of each step"
         except Exception as e:
             log(f"graph replay unavailable ({e}); timing eager launches")
     log(f"ms per step: {ms_per_step:.4f} ({timing}); eager {ms_per_step_eager:.4f}")
 
-    # Pass 3 (mean launch duration for the roofline): the step's GEMM (or
-    # fused) launches alone, the quantizer launches left out (their outputs
-    # are already in HBM), captured as one HIP graph per weight copy and
-    # replayed `steps` times between two HIP events on the launch stream, so
-    # the launches run back to back as in the timed steps and no event sits
-    # between two of them.  Falls back to the eager pass's per-launch events.
-    gemm_graph_us = None
-    if timing.startswith("HIP graph"):
-        try:
-            ggraphs = []
-            for i in range(ncopies):
-                gr = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gr):
-                    launch_step(pool[i], gemm_only=True)
-                ggraphs.append(gr)
-            for i in range(args.warmup):
-                ggraphs[i % ncopies].replay()
-            torch.cuda.synchronize()
-            h0, h1 = HipEvent(), HipEvent()
-            torch.cuda._sleep(int(2.4e9 * spin_s))
-            h0.record(stream_ptr)
-            for i in range(args.steps):
-                ggraphs[i % ncopies].replay()
-            h1.record(stream_ptr)
-            torch.cuda.synchronize()
-            gemm_graph_us = h0.elapsed_time(h1) * 1e3 / (args.steps * nr)
-            log(f"GEMM launches alone, graph replays: {gemm_graph_us:.3f} us per launch")
-        except Exception as e:
-            log(f"GEMM-only graph unavailable ({e}); launch durations from the eager pass")
-
+    # Pass 3 (mean launch durations for the roofline): for each launch group,
+    # the step's GEMM (or fused) launches of that group alone, the quantizer
+    # launches left out (their outputs are already in HBM), as HIP graphs
+    # replayed back to back between two HIP events.  Falls back to the eager
+    # pass's per-launch events.
     gemm_us = np.array(per_step_gemm) * 1e3
     med_us = np.median(gemm_us, axis=0)
     mean_us = gemm_us.mean(axis=0)
     p10_us, p90_us = np.percentile(gemm_us, 10, axis=0), np.percentile(gemm_us, 90, axis=0)
-    step_bytes = sum(w4a16_bytes(m, n, k, g) if args.w4a16 else
-                     algo_bytes(m, n, k, g) + quant_bytes(m, k) for (m, _, n, k, g, _) in runs)
-    step_ops = sum(2.0 * m * n * k for (m, _, n, k, g, _) in runs)
-    # bytes of the timed launch: a fused launch also reads A as fp16 and
-    # writes A8 and s_a instead of reading A8 and s_a (2MK more)
     gemm_bytes = np.array([w4a16_bytes(m, n, k, g) if args.w4a16 else
                            algo_bytes(m, n, k, g) + (2 * m * k if fused[r] else 0)
-                           for r, (m, _, n, k, g, _) in enumerate(runs)])
-    gemm_ops = np.array([2.0 * m * n * k for (m, _, n, k, g, _) in runs])
+                           for r, (m, _, n, k, g, _, _) in enumerate(runs)])
+    gemm_ops = np.array([2.0 * m * n * k for (m, _, n, k, g, _, _) in runs])
+    groups = {}
+    for name, (pred, bound, sources) in GROUPS.items():
+        sel = [r for r in range(nr) if pred(runs[r][0])]
+        if not sel:
+            continue
+        launch_us, how = float(mean_us[sel].mean()), "eager pass, HIP events around every launch"
+        if timing.startswith("HIP graph"):
+            try:
+                launch_us = graph_pass(sel, gemm_only=True) * 1e3 / len(sel)
+                how = "HIP graphs of the group's GEMM launches alone, HIP events around the replays"
+            except Exception as e:
+                log(f"GEMM-only graphs unavailable for {name} ({e}); eager durations")
+        groups[name] = {"runs": len(sel), "launch_us": launch_us, "how": how,
+                        "bytes": float(gemm_bytes[sel].mean()), "ops": float(gemm_ops[sel].mean()),
+                        "bound": bound, "sources": sources,
+                        "gemm_us_sum_median": float(med_us[sel].sum())}
+        log(f"group {name}: {len(sel)} runs, {launch_us:.3f} us per launch")
+
     table = []
-    for r, (m, layer, n, k, g, _) in enumerate(runs):
+    for r, (m, layer, n, k, g, _, _) in enumerate(runs):
         t = med_us[r] * 1e-6
         table.append({"m": m, "layer": layer, "n": n, "k": k, "g": g, "fused": fused[r],
                       "gemm_us_median": round(float(med_us[r]), 3),
@@ -427,27 +549,39 @@ def main():
         with open(args.runs_json, "w") as f:
             json.dump(table, f, indent=1)
 
-    # dominant kernel: the GEMM; average algorithmic bytes (or ops) per launch
-    # over average launch duration
-    avg_dur = (gemm_graph_us if gemm_graph_us is not None else float(mean_us.mean())) * 1e-6
-    hbm_bound = args.workload in ("llama3_8b_decode", "tiny") or max(r[0] for r in runs) <= 64
-    if hbm_bound:
-        achieved = float(gemm_bytes.mean()) / avg_dur / 1e9
-        peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
-    else:
-        achieved = float(gemm_ops.mean()) / avg_dur / 1e12
-        peak, unit, bound = INT8_PEAK_TOPS, "TFLOP/s", "mfma"
-    traffic = (None if (args.w4a16 or args.codebook or args.static_scale is not None)
-               else load_traffic(args.workload))
+    special = args.w4a16 or args.codebook or args.static_scale is not None
+
+    def roofline(name):
+        gr = groups[name]
+        dur = gr["launch_us"] * 1e-6
+        if gr["bound"] == "hbm":
+            achieved, peak, unit = gr["bytes"] / dur / 1e9, HBM_PEAK_GBS, "GB/s"
+        else:
+            achieved, peak, unit = gr["ops"] / dur / 1e12, INT8_PEAK_TOPS, "TFLOP/s"
+        return {"bound": gr["bound"], "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": None if special else load_traffic(args.workload, name),
+                "launches": f"{gr['runs']} per step ({name.replace('_', ' ')}), "
+                            f"{gr['launch_us']:.3f} us mean, {gr['how']}"}
+
+    # the dominant kernel (the most GEMM time per step) carries `roofline`;
+    # the other graded regime is reported beside it
+    graded = [name for name in groups if groups[name]["bound"] is not None]
+    dominant = max(graded, key=lambda nm: groups[nm]["gemm_us_sum_median"])
+    step_bytes = sum(w4a16_bytes(m, n, k, g) if args.w4a16 else
+                     algo_bytes(m, n, k, g) + quant_bytes(m, k)
+                     for (m, _, n, k, g, _, _) in runs)
     value_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     value_tops = step_ops / (ms_per_step * 1e-3) / 1e12
-    if hbm_bound:
+    if groups[dominant]["bound"] == "hbm":
         metric_value, metric_unit = value_gbs, "GB/s"
     else:
         metric_value, metric_unit = value_tops, "TOPS"
 
+    names = {"m1_to_4096": "Llama-3-8B layers at M = 1, 4, 16, 64, 256, 1024 and Qwen1.5-72B "
+                           "layers at M = 2048, 4096, g = 128 (M = 1..4096)"}
     result = {
-        "metric": "W4A8 GEMM TOPS + HBM GB/s vs roofline at M=1..4096 (Llama-3-8B layer shapes)",
+        "metric": METRIC,
         "value": round(metric_value, 2),
         "unit": metric_unit,
         "n_gpus": 1,
@@ -461,7 +595,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": args.workload,
-            "runs": [f"M={m} {layer} N={n} K={k} g={g}" for (m, layer, n, k, g, _) in runs],
+            "description": names.get(args.workload, args.workload),
+            "runs": [f"M={m} {layer} N={n} K={k} g={g}" for (m, layer, n, k, g, _, _) in runs],
             "step": "every run: w4a8_linear fused (one launch) where it applies, "
                     "else w4a8_quant_act + w4a8_gemm",
             "fused_runs": int(sum(fused)),
@@ -469,23 +604,26 @@ def main():
             "activation_scale": ("fp16 activations (W4A16 comparison)" if args.w4a16 else
                                  "static per-tensor %g" % args.static_scale
                                  if args.static_scale is not None else "per-token dynamic"),
-            "weight_rotation_copies": ncopies,
+            "weight_rotation": f"every layer use takes the next of >= {args.rotation_mib:g} MiB "
+                               f"of that layer's copies ({pool_bytes / 2**30:.2f} GiB in all)",
             "timing": timing,
-            "launch_durations": ("HIP graph of the step's GEMM launches alone, HIP events around its replays"
-                                 if gemm_graph_us is not None else
-                                 "separate eager pass, HIP events around every GEMM launch"),
             "parallelism": "single GPU",
         },
         "tops": round(value_tops, 3),
         "gbps": round(value_gbs, 2),
         "ms_per_step_eager": round(ms_per_step_eager, 4),
-        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
+        "regimes": {name: {"runs": gr["runs"], "gemm_launch_us_mean": round(gr["launch_us"], 3),
+                           "GB/s": round(gr["bytes"] / (gr["launch_us"] * 1e-6) / 1e9, 1),
+                           "TOPS": round(gr["ops"] / (gr["launch_us"] * 1e-6) / 1e12, 2)}
+                    for name, gr in groups.items()},
+        "roofline": roofline(dominant),
     }
+    for name in graded:
+        if name != dominant:
+            result["roofline_" + groups[name]["bound"]] = roofline(name)
     if not args.no_cpu_baseline:
-        sample_runs = [r for r in runs]
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(sample_runs, weights, metric_unit)
+        result["cpu_baseline"] = cpu_baseline(runs, weights, acts_host, metric_unit)
     print(json.dumps(result), flush=True)
 
 

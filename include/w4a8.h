@@ -249,6 +249,21 @@ w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
  * the call would be rejected.  Host only, no HIP call. */
 int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_opts* opts);
 
+/* ------------------------------------------------------- measurement aid
+ * Not part of the layer.  A read-only stream over `bytes` of device memory
+ * (16-byte aligned, a multiple of 16) by `workgroups` x 512 threads, with
+ * four non-temporal 16-byte loads in flight per thread: the practical HBM
+ * read ceiling that the weight-streaming regime (the FLUTE page, abstract:
+ * at small batch, moving the weights from global memory dominates) is
+ * measured against.  sink_dev holds `workgroups` uint32 values that are
+ * written only in the rare case a workgroup's folded value equals a fixed
+ * constant (so the loads cannot be optimised away); their contents mean
+ * nothing.  bytes == 0 is a no-op.
+ * Errors: INVALID_ARGUMENT (null pointer, misaligned or ragged size,
+ * workgroups outside 1..65536), DEVICE. */
+w4a8_status w4a8_read_probe(const void* src_dev, size_t bytes, int workgroups,
+                            uint32_t* sink_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,7 +51,16 @@ def workloads() -> dict[str, list[tuple]]:
     runs["group_sweep"] = [
         ("group_sweep", m, "gate_up", n, k, g, "student_t4")
         for m in (1, 32, 512) for g in (32, 64, 128, 0)]
+    # the metric's whole range in one step: decode, batched serving and the
+    # large-batch layers (each run keeps the seeds of the workload it comes
+    # from, named in its first field)
+    runs["m1_to_4096"] = (runs["llama3_8b_decode"] + runs["llama3_8b_batched"]
+                          + runs["qwen15_72b_large"])
     return runs
+
+
+# workloads made of the runs of others
+COMPOSITE = ("m1_to_4096",)
 
 
 def weight_seed(config_idx: int, shape_idx: int, g_idx: int) -> int:

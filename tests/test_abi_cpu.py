@@ -401,3 +401,15 @@ def test_w4a16_validates_before_any_hip_call():
                         None) == 1                                                    # > 8 waves
     assert L.w4a16_gemm(None, 512, 0, 512, None, 256, 128, None, 256, None, None) == 0
 
+
+
+def test_read_probe_validates_before_any_hip_call():
+    L = w4.lib
+    fake = ctypes.c_void_p(4096)
+    assert L.w4a8_read_probe(fake, 0, 256, fake, None) == 0          # nothing to read
+    assert L.w4a8_read_probe(None, 4096, 256, fake, None) == 1
+    assert L.w4a8_read_probe(fake, 4096, 256, None, None) == 1
+    assert L.w4a8_read_probe(fake, 4104, 256, fake, None) == 1       # not a multiple of 16
+    assert L.w4a8_read_probe(ctypes.c_void_p(4104), 4096, 256, fake, None) == 1   # misaligned
+    assert L.w4a8_read_probe(fake, 4096, 0, fake, None) == 1
+    assert L.w4a8_read_probe(fake, 4096, 65537, fake, None) == 1

@@ -334,7 +334,7 @@ def test_gemm_empty_batch_is_noop():
 def _full_runs():
     runs = []
     for cfg_idx, (name, items) in enumerate(synth.workloads().items()):
-        if name == "tiny":
+        if name == "tiny" or name in synth.COMPOSITE:
             continue
         layers = {}
         for (_, m, layer, n, k, g, dist) in items:

@@ -78,6 +78,7 @@ def _load():
         "w4a8_linear": (I, [P, I, I, I, P, I, I, P, I, P, I, P, P, I, P, Z, P, P]),
         "w4a8_linear_launches": (I, [I, I, I, I, P]),
         "w4a16_gemm": (I, [P, I, I, I, P, I, I, P, I, P, P]),
+        "w4a8_read_probe": (I, [P, Z, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -282,3 +283,13 @@ def w4a16(a, blob_dev, n: int, k: int, g: int, y=None, variant: int = 0, k_split
                           ctypes.byref(opts) if opts is not None else None, _stream_ptr(stream)),
            "w4a16_gemm")
     return y
+
+
+def read_probe(buf, offset: int, nbytes: int, workgroups: int, sink, stream=None):
+    """Measurement aid: a read-only stream over nbytes of the uint8 CUDA tensor
+    `buf` from byte `offset` (w4a8_read_probe); sink is an int32 CUDA tensor of
+    at least `workgroups` elements."""
+    assert buf.is_cuda and 0 <= offset and offset + nbytes <= buf.numel() * buf.element_size()
+    assert sink.numel() >= workgroups
+    _check(lib.w4a8_read_probe(buf.data_ptr() + offset, nbytes, workgroups, sink.data_ptr(),
+                               _stream_ptr(stream)), "w4a8_read_probe")

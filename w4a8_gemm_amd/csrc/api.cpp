@@ -432,6 +432,16 @@ extern "C" int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_
   return plan_gemm(m, n, k, opts).slices > 1 ? 3 : 2;
 }
 
+extern "C" w4a8_status w4a8_read_probe(const void* src_dev, size_t bytes, int workgroups,
+                                       uint32_t* sink_dev, void* stream) {
+  if (bytes == 0) return W4A8_OK;
+  if (!src_dev || !sink_dev || bytes % 16 || !aligned16(src_dev) || workgroups < 1 ||
+      workgroups > 65536)
+    return W4A8_ERR_INVALID_ARGUMENT;
+  return device_status(
+      launch_read_probe(src_dev, bytes, workgroups, sink_dev, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char* w4a8_last_device_error(void) {
   return t_last_hip_error == hipSuccess ? "no error" : hipGetErrorString(t_last_hip_error);
 }

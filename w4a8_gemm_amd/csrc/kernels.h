@@ -125,4 +125,9 @@ hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, in
                              const SkinnyConfig& c, hipStream_t stream);
 bool tiled_config_supported(const TiledConfig& c);
 
+// Read-only stream over `bytes` (a multiple of 16) with `workgroups` x 512
+// threads (probe.hip); a measurement aid, not part of the layer.
+hipError_t launch_read_probe(const void* src, size_t bytes, int workgroups, uint32_t* sink,
+                             hipStream_t stream);
+
 }  // namespace w4a8
