@@ -198,6 +198,30 @@ w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
                       void* workspace_dev, size_t workspace_bytes,
                       const w4a8_gemm_opts* opts, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): w4a8_gemm
+ * with no workspace argument.  When the plan splits K over workgroups, the
+ * int32 partial sums go to one static device array of W4A8_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends;
+ * nothing is allocated or freed by the call.
+ *   - Arguments and results are as for w4a8_gemm (bit-identical outputs).
+ *   - The automatic plan narrows its K split until the partial sums
+ *     (slices * m * n * 4 bytes) fit the array; a split forced through
+ *     opts->slices that does not fit returns W4A8_ERR_BUFFER_TOO_SMALL.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that
+ *     overlap in time on one GPU (other streams, other threads) race on it:
+ *     order them on one stream.
+ *   - The first call on each device looks the array's address up
+ *     (hipGetSymbolAddress, a host-side query); make that first call
+ *     outside stream capture.
+ * m == 0 is a no-op.  Errors as w4a8_gemm. */
+#define W4A8_SCRATCH_BYTES (64u << 20)
+w4a8_status w4a8_gemm_noalloc(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
+                              int m, const void* blob_dev, int n, int k, int g,
+                              uint16_t* y_dev, int ldy, int32_t* acc_dev, int ldacc,
+                              const w4a8_gemm_opts* opts, void* stream);
+
 /* ------------------------------------------------------------ whole layer
  * The W4A8 linear layer from fp16 activations: per-token quantization of A
  * (as w4a8_quant_act) followed by the GEMM (as w4a8_gemm), with A8 and s_a

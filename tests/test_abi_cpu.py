@@ -413,3 +413,25 @@ def test_read_probe_validates_before_any_hip_call():
     assert L.w4a8_read_probe(ctypes.c_void_p(4104), 4096, 256, fake, None) == 1   # misaligned
     assert L.w4a8_read_probe(fake, 4096, 0, fake, None) == 1
     assert L.w4a8_read_probe(fake, 4096, 65537, fake, None) == 1
+
+
+def test_gemm_noalloc_validates_before_any_hip_call():
+    """The allocation-free GEMM checks its arguments, and that a forced K
+    split fits the static scratch, before any HIP call."""
+    L = w4.lib
+    fake = ctypes.c_void_p(4096)
+    # (a8, lda8, s_a, m, blob, n, k, g, y, ldy, acc, ldacc, opts, stream)
+    assert L.w4a8_gemm_noalloc(None, 512, None, 0, None, 256, 512, 128, None, 256, None, 0,
+                               None, None) == 0                                  # m == 0
+    assert L.w4a8_gemm_noalloc(fake, 512, fake, 4, fake, 250, 512, 128, fake, 256, None, 0,
+                               None, None) == 2                                  # n % 16
+    assert L.w4a8_gemm_noalloc(None, 512, fake, 4, fake, 256, 512, 128, fake, 256, None, 0,
+                               None, None) == 1
+    assert L.w4a8_gemm_noalloc(fake, 520, fake, 4, fake, 256, 512, 128, fake, 256, None, 0,
+                               None, None) == 1                                  # lda8 % 16
+    opts = w4.GemmOpts(0, 0, 0, 0, 0, 0, 2)
+    assert L.w4a8_gemm_noalloc(fake, 8192, fake, 4096, fake, 4096, 8192, 128, fake, 4096, None,
+                               0, ctypes.byref(opts), None) == 3    # 2 x 64 MiB of partial sums
+    opts = w4.GemmOpts(1)
+    assert L.w4a8_gemm_noalloc(fake, 8192, fake, 100, fake, 4096, 8192, 128, fake, 4096, None,
+                               0, ctypes.byref(opts), None) == 2    # skinny: at most 64 rows

@@ -79,6 +79,7 @@ def _load():
         "w4a8_linear_launches": (I, [I, I, I, I, P]),
         "w4a16_gemm": (I, [P, I, I, I, P, I, I, P, I, P, P]),
         "w4a8_read_probe": (I, [P, Z, I, P, P]),
+        "w4a8_gemm_noalloc": (I, [P, I, P, I, P, I, I, I, P, I, P, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -228,6 +229,25 @@ def gemm(a8, s_a, blob_dev, n: int, k: int, g: int, y=None, acc=None, want_acc=F
                        workspace.numel() if workspace is not None else 0,
                        ctypes.byref(opts) if opts is not None else None, _stream_ptr(stream))
     _check(st, "w4a8_gemm")
+    return (y, acc) if acc is not None else y
+
+
+def gemm_noalloc(a8, s_a, blob_dev, n: int, k: int, g: int, y, acc=None, slices: int = 0,
+                 stream=None):
+    """w4a8_gemm_noalloc: the GEMM with no workspace argument (a K split keeps
+    its partial sums in the library's static device scratch).  y (and acc,
+    if given) must be preallocated; nothing is allocated here."""
+    torch = _torch()
+    m = a8.shape[0]
+    assert a8.dtype == torch.int8 and a8.is_cuda and a8.stride(1) == 1
+    opts = GemmOpts(0, 0, 0, 0, 0, 0, slices) if slices else None
+    st = lib.w4a8_gemm_noalloc(a8.data_ptr(), a8.stride(0), s_a.data_ptr(), m,
+                               blob_dev.data_ptr(), n, k, g, y.data_ptr(), y.stride(0),
+                               acc.data_ptr() if acc is not None else None,
+                               acc.stride(0) if acc is not None else 0,
+                               ctypes.byref(opts) if opts is not None else None,
+                               _stream_ptr(stream))
+    _check(st, "w4a8_gemm_noalloc")
     return (y, acc) if acc is not None else y
 
 

@@ -47,7 +47,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     steps = []
     for src in ("fused.hip", "skinny.hip", "tiled.hip", "quant_act.hip", "w4a16.hip",
-                "probe.hip"):
+                "probe.hip", "scratch.hip"):
         obj = os.path.join(BUILD, src + ".o")
         steps.append((obj, [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
     obj = os.path.join(BUILD, "api.cpp.o")

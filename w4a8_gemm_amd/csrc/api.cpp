@@ -179,6 +179,7 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     c.stages = (c.rw == 2 || (c.mr == 4 && c.kg == 1)) ? 3 : 2;
     if (opts->stages > 0) c.stages = opts->stages;
     if (opts->n_tiles > 0) c.nc = opts->n_tiles;
+
   } else if (t256 >= 224) {
     c = TiledConfig{8, 4, 4, 2, 1, 3};
   } else if ((m <= 64 || (m <= 128 && kblocks <= 128)) && kblocks >= 64 &&
@@ -226,12 +227,18 @@ namespace {
 // it launches the quantizer, so a call the GEMM would reject leaves no
 // kernel behind.  m > 0; a8/s_a may be checked by the caller instead (the
 // fused layer writes them).
-w4a8_status check_gemm(const Plan& pl, int k, int g, void* workspace_dev, size_t workspace_bytes) {
+w4a8_status check_plan(const Plan& pl, int k, int g) {
   if (pl.status != W4A8_OK) return pl.status;
   const int gpb = groups_per_block(k, g);
   if (pl.variant == 1 && !skinny_config_supported(pl.skinny, k, gpb))
     return W4A8_ERR_INVALID_ARGUMENT;
   if (pl.variant == 2 && !tiled_config_supported(pl.tiled)) return W4A8_ERR_INVALID_ARGUMENT;
+  return W4A8_OK;
+}
+
+w4a8_status check_gemm(const Plan& pl, int k, int g, void* workspace_dev, size_t workspace_bytes) {
+  const w4a8_status st = check_plan(pl, k, g);
+  if (st != W4A8_OK) return st;
   if (pl.workspace) {
     if (!workspace_dev || workspace_bytes < pl.workspace) return W4A8_ERR_BUFFER_TOO_SMALL;
     if (!aligned16(workspace_dev)) return W4A8_ERR_INVALID_ARGUMENT;
@@ -239,25 +246,22 @@ w4a8_status check_gemm(const Plan& pl, int k, int g, void* workspace_dev, size_t
   return W4A8_OK;
 }
 
-}  // namespace
+// The pointer and size checks shared by w4a8_gemm and w4a8_gemm_noalloc
+// (m > 0).
+bool gemm_args_ok(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev, const void* blob_dev,
+                  int n, int k, const uint16_t* y_dev, int ldy, const int32_t* acc_dev,
+                  int ldacc) {
+  if (!a8_dev || !s_a_dev || !blob_dev || !y_dev) return false;
+  if (lda8 < k || lda8 % 16 || ldy < n || (acc_dev && ldacc < n)) return false;
+  return aligned16(a8_dev) && aligned16(blob_dev);
+}
 
-extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev, int m,
-                                 const void* blob_dev, int n, int k, int g, uint16_t* y_dev,
-                                 int ldy, int32_t* acc_dev, int ldacc, void* workspace_dev,
-                                 size_t workspace_bytes, const w4a8_gemm_opts* opts,
-                                 void* stream) {
-  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
-  if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
-  if (m == 0) return W4A8_OK;
-  if (!a8_dev || !s_a_dev || !blob_dev || !y_dev) return W4A8_ERR_INVALID_ARGUMENT;
-  if (lda8 < k || lda8 % 16 || ldy < n || (acc_dev && ldacc < n)) return W4A8_ERR_INVALID_ARGUMENT;
-  if (!aligned16(a8_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
-
-  const Plan pl = plan_gemm(m, n, k, opts);
-  const w4a8_status st = check_gemm(pl, k, g, workspace_dev, workspace_bytes);
-  if (st != W4A8_OK) return st;
+// Enqueue a checked plan; `part` is the K-split partial-sum buffer (the
+// workspace, or the static scratch) when the plan splits K.
+w4a8_status run_gemm(const Plan& pl, const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
+                     int m, const void* blob_dev, int n, int k, int g, uint16_t* y_dev, int ldy,
+                     int32_t* acc_dev, int ldacc, void* part, hipStream_t s) {
   const int gpb = groups_per_block(k, g);
-
   Sections sec = sections(n, k, g);
   const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
   GemmParams p;
@@ -281,19 +285,86 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
   p.a8_out = nullptr;
   p.s_a_out = nullptr;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (pl.variant == 1) {
     e = launch_gemm_skinny(p, gpb, pl.skinny, s);
   } else {
     if (pl.slices > 1) {
-      p.part = static_cast<int32_t*>(workspace_dev);
+      p.part = static_cast<int32_t*>(part);
       p.kb_per_slice = pl.kb_per_slice;
     }
     e = launch_gemm_tiled(p, gpb, pl.tiled, pl.slices, s);
     if (e == hipSuccess && pl.slices > 1) e = launch_split_reduce(p, pl.slices, s);
   }
   return device_status(e);
+}
+
+}  // namespace
+
+extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev, int m,
+                                 const void* blob_dev, int n, int k, int g, uint16_t* y_dev,
+                                 int ldy, int32_t* acc_dev, int ldacc, void* workspace_dev,
+                                 size_t workspace_bytes, const w4a8_gemm_opts* opts,
+                                 void* stream) {
+  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
+  if (m == 0) return W4A8_OK;
+  if (!gemm_args_ok(a8_dev, lda8, s_a_dev, blob_dev, n, k, y_dev, ldy, acc_dev, ldacc))
+    return W4A8_ERR_INVALID_ARGUMENT;
+  const Plan pl = plan_gemm(m, n, k, opts);
+  const w4a8_status st = check_gemm(pl, k, g, workspace_dev, workspace_bytes);
+  if (st != W4A8_OK) return st;
+  return run_gemm(pl, a8_dev, lda8, s_a_dev, m, blob_dev, n, k, g, y_dev, ldy, acc_dev, ldacc,
+                  workspace_dev, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// The automatic plan with its K split narrowed until the partial sums fit
+// the static scratch (every split gives the same int32 sums); a forced
+// split that does not fit is left as it is and rejected by the caller.
+Plan plan_gemm_in_scratch(int m, int n, int k, const w4a8_gemm_opts* opts) {
+  Plan pl = plan_gemm(m, n, k, opts);
+  if (pl.status != W4A8_OK || pl.workspace <= kScratchBytes || (opts && opts->slices > 0))
+    return pl;
+  const int kblocks = k / kKBlock;
+  const size_t plane = size_t(m) * size_t(n) * 4u;
+  int slices = int(kScratchBytes / plane);        // the most that fit (0 or 1: none)
+  if (slices <= 1) {
+    pl.slices = 1;
+    pl.kb_per_slice = kblocks;
+    pl.workspace = 0;
+    return pl;
+  }
+  slices = std::min(slices, pl.slices);
+  pl.kb_per_slice = (kblocks + slices - 1) / slices;
+  pl.slices = (kblocks + pl.kb_per_slice - 1) / pl.kb_per_slice;   // none empty
+  pl.workspace = pl.slices > 1 ? size_t(pl.slices) * plane : 0;
+  return pl;
+}
+
+}  // namespace
+
+extern "C" w4a8_status w4a8_gemm_noalloc(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev,
+                                         int m, const void* blob_dev, int n, int k, int g,
+                                         uint16_t* y_dev, int ldy, int32_t* acc_dev, int ldacc,
+                                         const w4a8_gemm_opts* opts, void* stream) {
+  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
+  if (m == 0) return W4A8_OK;
+  if (!gemm_args_ok(a8_dev, lda8, s_a_dev, blob_dev, n, k, y_dev, ldy, acc_dev, ldacc))
+    return W4A8_ERR_INVALID_ARGUMENT;
+  const Plan pl = plan_gemm_in_scratch(m, n, k, opts);
+  const w4a8_status st = check_plan(pl, k, g);
+  if (st != W4A8_OK) return st;
+  if (pl.workspace > kScratchBytes) return W4A8_ERR_BUFFER_TOO_SMALL;   // a forced split
+  void* part = nullptr;
+  if (pl.workspace) {
+    hipError_t e = scratch_address(&part);
+    if (e != hipSuccess) return device_status(e);
+  }
+  return run_gemm(pl, a8_dev, lda8, s_a_dev, m, blob_dev, n, k, g, y_dev, ldy, acc_dev, ldacc,
+                  part, static_cast<hipStream_t>(stream));
 }
 
 namespace {

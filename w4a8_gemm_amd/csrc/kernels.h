@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "../../include/w4a8.h"
+
 namespace w4a8 {
 
 struct GemmParams {
@@ -124,6 +126,12 @@ bool fused_config_supported(const SkinnyConfig& c, int m, int k);
 hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, int gpb,
                              const SkinnyConfig& c, hipStream_t stream);
 bool tiled_config_supported(const TiledConfig& c);
+
+// The static scratch buffer of w4a8_gemm_noalloc (scratch.hip): bytes per
+// device, and its device address for the current device (looked up once
+// per device by hipGetSymbolAddress).
+constexpr size_t kScratchBytes = W4A8_SCRATCH_BYTES;
+hipError_t scratch_address(void** ptr);
 
 // Read-only stream over `bytes` (a multiple of 16) with `workgroups` x 512
 // threads (probe.hip); a measurement aid, not part of the layer.
