@@ -72,7 +72,21 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
     aptr[i] = p.a8 + size_t(min(row, p.m - 1)) * p.lda8 + 16 * quarter;
   }
 
-  const EpiScales<MR, NC> es = load_scales<MR, NC>(p, row_tile0, tile0, lane);
+  // Epilogue scales: the column scales now; the row scales too, except for
+  // 64-row tiles, whose 16 row scales per lane would stay live through the
+  // whole K loop beside the ring: those load before the last ring group.
+  EpiScales<MR, NC> es;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) es.s1[c] = h2f(p.s1[min((tile0 + c) * 16 + (lane & 15), p.n - 1)]);
+  auto load_row_scales = [&]() {
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        es.sa[i][r] = h2f(p.s_a[min((row_tile0 + i) * 16 + 4 * (lane >> 4) + r, p.m - 1)]);
+  };
+  constexpr bool kLateRowScales = MR > 2;
+  if constexpr (!kLateRowScales) load_row_scales();
 
   v4i acc[MR][NC];
 #pragma unroll
@@ -169,10 +183,13 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
       }
       next_group_meta();
     }
+    if constexpr (kLateRowScales) load_row_scales();
     // last group: no further loads
 #pragma unroll
     for (int j = 0; j < D; ++j)
       if (kb0 + j < kb_end) compute(j, kb0 + j);
+  } else if constexpr (kLateRowScales) {
+    load_row_scales();
   }
 
   constexpr int F = MR * NC;
