@@ -308,6 +308,9 @@ def main():
                          "table decode) instead of the workload's group size")
     ap.add_argument("--stream-probe", action="store_true",
                     help="time the read-only HBM stream probe instead of the layer")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device-to-device copy five times (the known-size "
+                         "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
@@ -323,6 +326,17 @@ def main():
         sys.exit(2)
     if args.stream_probe:
         stream_probe(args)
+        return
+    if args.copy_calibration:
+        import torch
+        nbytes = 256 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                          "copies": 5}), flush=True)
         return
 
     import torch

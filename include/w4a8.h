@@ -76,6 +76,15 @@ typedef enum {
 #define W4A8_N_QUANTUM 16
 #define W4A8_K_MAX 131072
 
+/* Upper bounds on the other sizes, so that every launch's grid and every
+ * index fits its integer type: tokens m <= W4A8_M_MAX (and output columns
+ * n <= W4A8_N_MAX) in every entry point, and rows of at most
+ * W4A8_ACT_K_MAX values in the activation quantizers.  Larger sizes are
+ * rejected (INVALID_ARGUMENT for m and the quantizers' k, UNSUPPORTED for n). */
+#define W4A8_M_MAX (1 << 22)
+#define W4A8_N_MAX (1 << 22)
+#define W4A8_ACT_K_MAX (1 << 30)
+
 const char* w4a8_status_string(w4a8_status s);
 
 /* Text of the HIP error behind the most recent W4A8_ERR_DEVICE returned to
@@ -124,10 +133,10 @@ w4a8_status w4a8_unpack(const void* blob, size_t blob_bytes,
 /* ----------------------------------------------------- activation quantizer
  * Per-token int8 quantization of A (m x k fp16, row stride lda elements) into
  * a8_dev (m x k int8, row stride lda8 bytes) and s_a_dev (m fp16 scales).
- * m == 0 is a no-op.  k may be any positive size.  NaN/inf inputs give
+ * m == 0 is a no-op.  k is any size from 1 to W4A8_ACT_K_MAX.  NaN/inf inputs give
  * unspecified outputs (no device-side check).
- * Errors: INVALID_ARGUMENT (null pointer, m < 0, k <= 0, lda < k, lda8 < k),
- * DEVICE. */
+ * Errors: INVALID_ARGUMENT (null pointer, m < 0, k <= 0, lda < k, lda8 < k,
+ * m > W4A8_M_MAX, k > W4A8_ACT_K_MAX), DEVICE. */
 w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
                            int8_t* a8_dev, int lda8, uint16_t* s_a_dev,
                            void* stream);

@@ -50,9 +50,10 @@ def build(verbose: bool = False) -> str:
                 "probe.hip", "scratch.hip"):
         obj = os.path.join(BUILD, src + ".o")
         steps.append((obj, [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
-    obj = os.path.join(BUILD, "api.cpp.o")
-    steps.append((obj, [HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "api.cpp"),
-                        "-o", obj]))
+    for src in ("api.cpp", "configs.cpp"):
+        obj = os.path.join(BUILD, src + ".o")
+        steps.append((obj, [HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src),
+                            "-o", obj]))
     gxx = shutil.which("g++") or "g++"
     obj = os.path.join(BUILD, "pack.cpp.o")
     steps.append((obj, [gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, "pack.cpp"), "-o", obj]))

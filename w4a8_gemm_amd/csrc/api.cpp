@@ -25,7 +25,7 @@ w4a8_status device_status(hipError_t e) {
 }
 
 bool gemm_shape_supported(int n, int k, int g) {
-  if (n % kColTile || k % kKBlock || k > W4A8_K_MAX) return false;
+  if (n % kColTile || k % kKBlock || k > W4A8_K_MAX || n > W4A8_N_MAX) return false;
   if (g == W4A8_GROUP_PER_CHANNEL || g == k || g == W4A8_CODEBOOK_NF) return true;
   return (g == 32 || g == 64 || g == 128) && k % g == 0;
 }
@@ -82,7 +82,8 @@ extern "C" const char* w4a8_status_string(w4a8_status s) {
 extern "C" w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int lda,
                                       int8_t* a8_dev, int lda8, uint16_t* s_a_dev,
                                       void* stream) {
-  if (m < 0 || k <= 0 || lda < k || lda8 < k) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m < 0 || m > W4A8_M_MAX || k <= 0 || k > W4A8_ACT_K_MAX || lda < k || lda8 < k)
+    return W4A8_ERR_INVALID_ARGUMENT;
   if (m == 0) return W4A8_OK;
   if (!a_dev || !a8_dev || !s_a_dev) return W4A8_ERR_INVALID_ARGUMENT;
   return device_status(launch_quant_act(a_dev, m, k, lda, a8_dev, lda8, s_a_dev,
@@ -92,7 +93,8 @@ extern "C" w4a8_status w4a8_quant_act(const uint16_t* a_dev, int m, int k, int l
 extern "C" w4a8_status w4a8_quant_act_static(const uint16_t* a_dev, int m, int k, int lda,
                                              uint16_t scale_f16, int8_t* a8_dev, int lda8,
                                              uint16_t* s_a_dev, void* stream) {
-  if (m < 0 || k <= 0 || lda < k || lda8 < k) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m < 0 || m > W4A8_M_MAX || k <= 0 || k > W4A8_ACT_K_MAX || lda < k || lda8 < k)
+    return W4A8_ERR_INVALID_ARGUMENT;
   // the scale must be a finite, non-negative fp16 value (sign bit clear,
   // exponent field not all ones)
   if ((scale_f16 & 0x8000u) || (scale_f16 & 0x7C00u) == 0x7C00u) return W4A8_ERR_INVALID_ARGUMENT;
@@ -117,11 +119,22 @@ struct Plan {
 
 // Workgroup tiles of rows x cols over the output.
 long tiled_tiles(int m, int n, int rows, int cols = 256) {
-  return long((m + rows - 1) / rows) * long((n + cols - 1) / cols);
+  return ((long(m) + rows - 1) / rows) * ((long(n) + cols - 1) / cols);
+}
+
+// Forced options outside the ranges any kernel takes (and negative values)
+// are rejected before they enter any size arithmetic.
+bool opts_in_range(const w4a8_gemm_opts* o) {
+  if (!o) return true;
+  return o->variant >= 0 && o->variant <= 3 && o->k_split >= 0 && o->k_split <= 8 &&
+         o->n_tiles >= 0 && o->n_tiles <= 4 && o->m_tiles >= 0 && o->m_tiles <= 16 &&
+         o->stages >= 0 && o->stages <= 8 && o->row_groups >= 0 && o->row_groups <= 2 &&
+         o->slices >= 0 && o->slices <= kMaxSlices && o->workgroups >= 0;
 }
 
 Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   Plan pl;
+  if (!opts_in_range(opts)) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
   pl.variant = opts ? opts->variant : 0;
   if (pl.variant < 0 || pl.variant > 2) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
   const int kblocks = k / kKBlock;
@@ -204,6 +217,12 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   }
   if (opts && opts->slices > 0) slices = opts->slices;
   if (slices > kMaxSlices) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
+  if (!tiled_config_supported(c)) { pl.status = W4A8_ERR_INVALID_ARGUMENT; return pl; }
+  // one launch holds every (tile, slice) workgroup
+  if (tiled_tiles(m, n, c.rw * 16 * c.mr, c.nw * c.nc * 16) * slices > kMaxWorkgroups) {
+    pl.status = W4A8_ERR_UNSUPPORTED;
+    return pl;
+  }
   slices = std::min(slices, kblocks);
   pl.kb_per_slice = (kblocks + slices - 1) / slices;
   pl.slices = (kblocks + pl.kb_per_slice - 1) / pl.kb_per_slice;   // none empty
@@ -215,7 +234,7 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
 
 extern "C" size_t w4a8_gemm_workspace_size(int m, int n, int k, int g,
                                            const w4a8_gemm_opts* opts) {
-  if (m <= 0 || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
+  if (m <= 0 || m > W4A8_M_MAX || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
   const Plan pl = plan_gemm(m, n, k, opts);
   return pl.status == W4A8_OK ? pl.workspace : 0;
 }
@@ -306,7 +325,7 @@ extern "C" w4a8_status w4a8_gemm(const int8_t* a8_dev, int lda8, const uint16_t*
                                  int ldy, int32_t* acc_dev, int ldacc, void* workspace_dev,
                                  size_t workspace_bytes, const w4a8_gemm_opts* opts,
                                  void* stream) {
-  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m < 0 || m > W4A8_M_MAX || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
   if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   if (m == 0) return W4A8_OK;
   if (!gemm_args_ok(a8_dev, lda8, s_a_dev, blob_dev, n, k, y_dev, ldy, acc_dev, ldacc))
@@ -349,7 +368,7 @@ extern "C" w4a8_status w4a8_gemm_noalloc(const int8_t* a8_dev, int lda8, const u
                                          int m, const void* blob_dev, int n, int k, int g,
                                          uint16_t* y_dev, int ldy, int32_t* acc_dev, int ldacc,
                                          const w4a8_gemm_opts* opts, void* stream) {
-  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m < 0 || m > W4A8_M_MAX || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
   if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   if (m == 0) return W4A8_OK;
   if (!gemm_args_ok(a8_dev, lda8, s_a_dev, blob_dev, n, k, y_dev, ldy, acc_dev, ldacc))
@@ -404,7 +423,7 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
                                    int8_t* a8_dev, int lda8, uint16_t* s_a_dev, int32_t* acc_dev,
                                    int ldacc, void* workspace_dev, size_t workspace_bytes,
                                    const w4a8_gemm_opts* opts, void* stream) {
-  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m < 0 || m > W4A8_M_MAX || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
   if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   if (m == 0) return W4A8_OK;
   if (!a_dev || !blob_dev || !y_dev || !a8_dev || !s_a_dev) return W4A8_ERR_INVALID_ARGUMENT;
@@ -413,8 +432,7 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
   if (!aligned16(a_dev) || !aligned16(a8_dev) || !aligned16(blob_dev))
     return W4A8_ERR_INVALID_ARGUMENT;
   const int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant > 3 || (opts && opts->workgroups < 0))
-    return W4A8_ERR_INVALID_ARGUMENT;
+  if (variant < 0 || variant > 3 || !opts_in_range(opts)) return W4A8_ERR_INVALID_ARGUMENT;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const SkinnyConfig fc = fused_plan(m, n, k, opts);
@@ -457,13 +475,14 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
 extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
                                   const void* blob_dev, int n, int g, uint16_t* y_dev, int ldy,
                                   const w4a8_gemm_opts* opts, void* stream) {
-  if (m < 0 || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
+  if (m < 0 || m > W4A8_M_MAX || n <= 0 || k <= 0 || g < 0) return W4A8_ERR_INVALID_ARGUMENT;
   if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   if (m == 0) return W4A8_OK;
   if (!a_dev || !blob_dev || !y_dev) return W4A8_ERR_INVALID_ARGUMENT;
   if (lda < k || lda % 8 || ldy < n) return W4A8_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
-  if (opts && (opts->variant > 1 || opts->variant < 0)) return W4A8_ERR_INVALID_ARGUMENT;
+  if (opts && (opts->variant > 1 || opts->variant < 0 || !opts_in_range(opts)))
+    return W4A8_ERR_INVALID_ARGUMENT;
   if (m > 64 || g == W4A8_CODEBOOK_NF) return W4A8_ERR_UNSUPPORTED;
   // one row tile per workgroup (more row tiles go to grid.y): fp16 operands
   // take twice the registers of int8 ones, and a deeper row tile would spill
@@ -494,9 +513,9 @@ extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
 }
 
 extern "C" int w4a8_linear_launches(int m, int n, int k, int g, const w4a8_gemm_opts* opts) {
-  if (m <= 0 || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
+  if (m <= 0 || m > W4A8_M_MAX || n <= 0 || k <= 0 || !gemm_shape_supported(n, k, g)) return 0;
   const int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant > 3 || (opts && opts->workgroups < 0)) return 0;
+  if (variant < 0 || variant > 3 || !opts_in_range(opts)) return 0;
   const bool fused_ok = fused_config_supported(fused_plan(m, n, k, opts), m, k);
   if (variant == 3) return fused_ok ? 1 : 0;
   if (variant == 0 && fused_ok && fused_by_default(m, n, k)) return 1;

@@ -463,23 +463,6 @@ hipError_t fused_by_kbw(const GemmParams& p, const uint16_t* a, int lda, int gpb
 
 }  // namespace
 
-size_t fused_lds_bytes(int kw, int nc, int m, int kbw) {
-  const size_t red = kw > 1 ? 2 * size_t(kw) * nc * 1024 : 0;
-  return size_t(kw) * 64 + red + size_t(kw) * m * (size_t(kbw) * 128 + 16);
-}
-
-int fused_rows(int m) { return m <= 1 ? 1 : (m <= 2 ? 2 : (m <= 4 ? 4 : (m <= 8 ? 8 : 16))); }
-
-bool fused_config_supported(const SkinnyConfig& c, int m, int k) {
-  if (m < 1 || m > kFusedMaxRows || c.mr != 1) return false;
-  if (c.nc != 1 && c.nc != 2) return false;
-  if (c.kw < 1 || c.kw > 8 || !(c.kbw == 4 || c.kbw == 8 || c.kbw == 16)) return false;
-  if (c.kw * c.kbw * 128 < k) return false;
-  if (fused_rows(m) * c.kbw > kFusedMaxHold) return false;
-  if (c.wgs < 0) return false;
-  return fused_lds_bytes(c.kw, c.nc, m, c.kbw) <= kFusedMaxLds;
-}
-
 hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, int gpb,
                              const SkinnyConfig& c, hipStream_t stream) {
   if (!fused_config_supported(c, p.m, p.k)) return hipErrorInvalidValue;

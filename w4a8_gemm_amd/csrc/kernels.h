@@ -30,6 +30,7 @@ struct GemmParams {
 };
 
 constexpr int kMaxSlices = 16;   // workgroups splitting K of one tile
+constexpr long kMaxWorkgroups = (1L << 31) - 1;   // workgroups of one launch
 // 17..64 tokens with K >= 8192: from this many activations (M * K) on, 64 x
 // 128 tiles with K split over workgroups beat the skinny kernel, whose every
 // workgroup re-reads all of A8 (graph replays on MI355X: down projection
@@ -67,6 +68,9 @@ struct SkinnyConfig {
   int kbw;   // 128-k blocks per wave
   int wgs = 0;   // fused kernel: workgroups of the persistent grid (0: one per column-tile group)
 };
+
+// Waves along N in every tiled workgroup.
+constexpr int kTiledColGroups = 4;
 
 struct TiledConfig {
   int mr;       // 16-row tiles per wave
@@ -122,6 +126,8 @@ constexpr int kFusedAutoWgs = 256;
 constexpr int kFusedMaxHold = 64;
 constexpr size_t kFusedMaxLds = 128 * 1024;
 size_t fused_lds_bytes(int kw, int nc, int m, int kbw);
+// Rows of the fused kernel's tile: m rounded up to a power of two (1..16).
+int fused_rows(int m);
 bool fused_config_supported(const SkinnyConfig& c, int m, int k);
 hipError_t launch_gemm_fused(const GemmParams& p, const uint16_t* a, int lda, int gpb,
                              const SkinnyConfig& c, hipStream_t stream);

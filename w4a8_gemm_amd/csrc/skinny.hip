@@ -263,15 +263,6 @@ hipError_t skinny_by_gpb(const GemmParams& p, int gpb, const SkinnyConfig& c, hi
 
 }  // namespace
 
-bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb) {
-  const bool shape_ok = (c.mr == 1 && (c.nc == 1 || c.nc == 2 || c.nc == 4)) ||
-                        ((c.mr == 2 || c.mr == 4) && (c.nc == 1 || c.nc == 2));
-  if (!shape_ok) return false;
-  (void)gpb;
-  if (c.kw < 1 || c.kw > 8 || c.kbw < 1 || c.kbw % 4) return false;   // ring groups of 4
-  return c.kw * c.kbw * 128 >= k;                    // the waves cover all of K
-}
-
 hipError_t launch_gemm_skinny(const GemmParams& p, int gpb, const SkinnyConfig& c,
                               hipStream_t stream) {
   if (c.mr == 1 && c.nc == 1) return skinny_by_gpb<1, 1>(p, gpb, c, stream);

@@ -92,7 +92,7 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int* bm, int*
   *bn = in_group / gm;
 }
 
-constexpr int kColGroups = 4;   // waves along N per workgroup
+constexpr int kColGroups = kTiledColGroups;   // waves along N per workgroup
 constexpr int kTiledMaxLds = 160 * 1024;   // LDS of one gfx950 compute unit
 
 // One LDS stage: for each of the KG k-groups, the activation tile, weight
@@ -643,27 +643,6 @@ hipError_t tiled_by_gpb(const GemmParams& p, int gpb, int sl, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// Four-wave tiles (RW = KG = 1) and their pipeline depths.  Deeper
-// pipelines keep more k-blocks in flight per workgroup, which is what a
-// grid of about one workgroup per compute unit needs to cover the memory
-// latency; each depth fits the 160 KB of LDS and the vmcnt range.
-bool four_wave_stages_ok(int mr, int nc, int s) {
-  if (mr == 8 && nc == 4) return s >= 2 && s <= 4;
-  if (mr == 4 && nc == 4) return s >= 2 && s <= 5;
-  if (mr == 8 && nc == 2) return s >= 2 && s <= 6;
-  if (mr == 4 && nc == 2) return s == 2 || s == 3 || s == 4 || s == 6 || s == 8;
-  return false;
-}
-
-// Two k-groups of four waves (eight waves, KG = 2): the 256-column tiles
-// with 2 stages, the 128-column tiles deeper.
-bool two_group_stages_ok(int mr, int nc, int s) {
-  if (nc == 4) return (mr == 8 || mr == 4) && s == 2;
-  if (mr == 8 && nc == 2) return s == 2 || s == 3;
-  if (mr == 4 && nc == 2) return s >= 2 && s <= 4;
-  return false;
-}
-
 template <int MR, int NC>
 hipError_t four_wave_by_stages(const GemmParams& p, int gpb, int stages, int sl, hipStream_t s) {
   switch (stages) {
@@ -687,13 +666,6 @@ hipError_t four_wave_by_stages(const GemmParams& p, int gpb, int stages, int sl,
 }
 
 }  // namespace
-
-bool tiled_config_supported(const TiledConfig& c) {
-  if (c.nw != kColGroups) return false;
-  if (c.rw == 2) return c.kg == 1 && c.mr == 8 && c.nc == 4 && c.stages == 3;
-  if (c.kg == 2) return c.rw == 1 && two_group_stages_ok(c.mr, c.nc, c.stages);
-  return c.rw == 1 && c.kg == 1 && four_wave_stages_ok(c.mr, c.nc, c.stages);
-}
 
 hipError_t launch_gemm_tiled(const GemmParams& p, int gpb, const TiledConfig& c, int sl,
                              hipStream_t stream) {
