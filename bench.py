@@ -46,16 +46,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 CODEBOOK_NF = 1   # g value of the non-uniform codebook mode (no meta)
 
-# sources of the kernels each counter entry covers (small M: fused and
-# skinny; larger M: tiled with its K-split reduction)
-SKINNY_SOURCES = ["fused.hip", "skinny.hip", "gemm_common.h", "quant_common.h", "codebook.h"]
-TILED_SOURCES = ["tiled.hip", "gemm_common.h", "quant_common.h", "codebook.h"]
+# sources each counter entry covers: the kernels a group launches and the
+# plan that picks them (small M: fused and skinny; larger M: tiled with its
+# K-split reduction; 17..1023 tokens: skinny and tiled)
+_COMMON = ["gemm_common.h", "quant_common.h", "codebook.h", "api.cpp"]
+SKINNY_SOURCES = ["fused.hip", "skinny.hip"] + _COMMON
+TILED_SOURCES = ["tiled.hip"] + _COMMON
+MID_SOURCES = ["skinny.hip", "tiled.hip"] + _COMMON
 
 # launch groups whose mean duration is timed on its own: the two graded
 # regimes (M <= 16, HBM-bound; M >= 1024, MFMA-bound) and the transition
 GROUPS = {
     "m_le_16": (lambda m: m <= 16, "hbm", SKINNY_SOURCES),
-    "m_17_1023": (lambda m: 16 < m < 1024, None, TILED_SOURCES),
+    "m_17_1023": (lambda m: 16 < m < 1024, None, MID_SOURCES),
     "m_ge_1024": (lambda m: m >= 1024, "mfma", TILED_SOURCES),
 }
 
@@ -315,8 +318,8 @@ def main():
                     help="print the source hashes the HBM counter entries are keyed to")
     args = ap.parse_args()
     if args.print_source_hash:
-        for files in (SKINNY_SOURCES, TILED_SOURCES):
-            print(" + ".join(files), source_hash(files))
+        for name, (_, _, files) in GROUPS.items():
+            print(name, " + ".join(files), source_hash(files))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
