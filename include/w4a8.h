@@ -108,10 +108,19 @@ const char* w4a8_last_device_error(void);
  * The blob is position independent: copy it verbatim to device memory and
  * pass that copy to w4a8_gemm.  Device code never reads the header.       */
 
-/* Bytes of the blob for (n, k, g); 0 if the shape is unsupported. */
+/* Bytes of the blob for (n, k, g); 0 if the shape is unsupported.  (The
+ * blob layout above; the quantization it stores is w4a8_pack's.) */
 size_t w4a8_packed_size(int n, int k, int g);
 
 /* Quantize W (n x k fp32, row stride ldw >= k elements) and write the blob.
+ * Defining passages: the progressive quantization of the QServe/QoQ abstract
+ * (read as: weights first to int8 per output channel, then to 4 bits per
+ * group, so that dequantization in the W4A8 GEMM is cheap integer work), and
+ * the offline weight reordering of the same abstract (compute-aware
+ * reordering), the QUICK abstract (interleaving that skips the shared-memory
+ * write-back after dequantization) and the FLUTE page ("方法详解"): the codes
+ * are stored in the order the matrix-core operand wants them, so the kernel
+ * never rearranges them through shared memory.
  * Host only, synchronous, thread-safe.  n_threads <= 0 uses all hardware
  * threads; the output bytes do not depend on the thread count.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, BUFFER_TOO_SMALL, NONFINITE, RANGE. */
@@ -133,6 +142,9 @@ w4a8_status w4a8_unpack(const void* blob, size_t blob_bytes,
 /* ----------------------------------------------------- activation quantizer
  * Per-token int8 quantization of A (m x k fp16, row stride lda elements) into
  * a8_dev (m x k int8, row stride lda8 bytes) and s_a_dev (m fp16 scales).
+ * Defining passages: the 8-bit activations of the QServe/QoQ abstract, with
+ * the per-token dynamic scale that the PrefixQuant page ("Key Findings")
+ * names as the usual practice.
  * m == 0 is a no-op.  k is any size from 1 to W4A8_ACT_K_MAX.  NaN/inf inputs give
  * unspecified outputs (no device-side check).
  * Errors: INVALID_ARGUMENT (null pointer, m < 0, k <= 0, lda < k, lda8 < k,
@@ -155,6 +167,14 @@ w4a8_status w4a8_quant_act_static(const uint16_t* a_dev, int m, int k, int lda,
 
 /* -------------------------------------------------------------- W4A8 GEMM
  * Y = fp16(s_a[m] * s1[n] * sum_k A8[m,k] * W8^[n,k]) with int32 accumulation.
+ * Defining passages: the QServe/QoQ abstract (the int8 product runs on the
+ * matrix cores and no partial sum is dequantized), and the LiquidGEMM page
+ * ("Метод": each 4-bit weight is decoded to int8 in registers by a few
+ * integer instructions that cannot overflow, feeding the int8 MMA directly).
+ * Small M streams the weights (the FLUTE page's small-batch regime, abstract:
+ * moving weights from global memory dominates); large M is bound by the
+ * int8 matrix cores, the regime of the kernel speedups the LiquidGEMM page
+ * reports ("Результаты").
  *   a8_dev    m x k int8, row stride lda8 bytes (lda8 >= k, lda8 % 16 == 0,
  *             16-byte aligned)
  *   s_a_dev   m fp16 per-token scales
@@ -234,7 +254,10 @@ w4a8_status w4a8_gemm_noalloc(const int8_t* a8_dev, int lda8, const uint16_t* s_
 /* ------------------------------------------------------------ whole layer
  * The W4A8 linear layer from fp16 activations: per-token quantization of A
  * (as w4a8_quant_act) followed by the GEMM (as w4a8_gemm), with A8 and s_a
- * written to a8_dev / s_a_dev as well.  For up to 57344 activations
+ * written to a8_dev / s_a_dev as well.  Defining passage: the W4A8 layer of
+ * the QServe/QoQ abstract, 8-bit activations included; fusing the
+ * quantization into the small-M GEMM is this library's choice (it saves a
+ * launch where the whole GEMM takes a few microseconds).  For up to 57344 activations
  * (m * k; e.g. up to 14 tokens at k = 4096, 4 at k = 14336), or 65536 on
  * layers of at least 16384 columns, both steps run in one kernel:
  * each workgroup of a persistent grid quantizes the rows itself while its
@@ -261,7 +284,9 @@ w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
                         size_t workspace_bytes, const w4a8_gemm_opts* opts, void* stream);
 
 /* ----------------------------------------------------- W4A16 comparison
- * The weight-only baseline the pages measure W4A8 against, on the same blob:
+ * The weight-only baseline the pages measure W4A8 against (the AWQ-style
+ * W4A16 of the QServe/QoQ abstract, the mixed-precision kernels of the QUICK
+ * abstract, FLUTE's weight-only GEMM), here on the same blob:
  * fp16 activations times the fp16 weights W16^[n,k] = fp16(s1[n] * W8^[n,k])
  * (one rounding), summed in fp32 on the fp16 MFMA:
  *   Y[m,n] = fp16(sum_k A[m,k] * W16^[n,k])
