@@ -293,11 +293,15 @@ w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
  * There is no activation quantization and no s_a.
  *   a_dev   m x k fp16, row stride lda elements (lda >= k, lda % 8 == 0,
  *           16-byte aligned); y_dev m x n fp16, row stride ldy >= n.
- *   opts    NULL, or variant 0/1 with n_tiles / k_split as for the skinny
- *           W4A8 kernel.
- * Small M only (M <= 64, the weight-streaming regime).  Results are within
- * the fp32 summation bound of the exact sum, not bit-exact across choices.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (shape, or m > 64), DEVICE. */
+ *   opts    NULL for the automatic choice (the skinny kernel up to 64
+ *           tokens, and up to 128 where the tiled grid would hold fewer than
+ *           128 tiles; the tiled one above); variant 1 forces the skinny
+ *           kernel (m <= 128; n_tiles / k_split as for the skinny W4A8
+ *           kernel), variant 2 the tiled kernel (256 x 128 tiles, any m).
+ * Results are within the fp32 summation bound of the exact sum, not
+ * bit-exact across choices.  The codebook mode is not supported.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (shape, codebook blob, variant 1
+ * with m > 128), DEVICE. */
 w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
                        const void* blob_dev, int n, int g, uint16_t* y_dev, int ldy,
                        const w4a8_gemm_opts* opts, void* stream);

@@ -26,6 +26,7 @@ hipError_t launch_split_reduce(const GemmParams&, int, hipStream_t) { return hip
 hipError_t launch_w4a16_skinny(const Gemm16Params&, int, const SkinnyConfig&, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_w4a16_tiled(const Gemm16Params&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_gemm_fused(const GemmParams&, const uint16_t*, int, int, const SkinnyConfig&,
                              hipStream_t) {
   return hipErrorNoDevice;

@@ -387,15 +387,18 @@ def test_w4a16_validates_before_any_hip_call():
     fake = ctypes.c_void_p(4096)
     # (a, lda, m, k, blob, n, g, y, ldy, opts, stream)
     assert L.w4a16_gemm(fake, 512, 4, 512, fake, 250, 128, fake, 256, None, None) == 2   # n % 16
-    assert L.w4a16_gemm(fake, 512, 65, 512, fake, 256, 128, fake, 256, None, None) == 2  # m > 64
+    opts = w4.GemmOpts(1)
+    assert L.w4a16_gemm(fake, 512, 129, 512, fake, 256, 128, fake, 256, ctypes.byref(opts),
+                        None) == 2                                                    # skinny, m > 128
+    assert L.w4a16_gemm(fake, 512, 65, 512, fake, 256, 1, fake, 256, None, None) == 2    # codebook
     assert L.w4a16_gemm(fake, 516, 4, 512, fake, 256, 128, fake, 256, None, None) == 1   # lda % 8
     assert L.w4a16_gemm(fake, 500, 4, 512, fake, 256, 128, fake, 256, None, None) == 1   # lda < k
     assert L.w4a16_gemm(None, 512, 4, 512, fake, 256, 128, fake, 256, None, None) == 1
     assert L.w4a16_gemm(ctypes.c_void_p(4104), 512, 4, 512, fake, 256, 128, fake, 256, None,
                         None) == 1                                                    # misaligned
-    opts = w4.GemmOpts(2)
+    opts = w4.GemmOpts(3)
     assert L.w4a16_gemm(fake, 512, 4, 512, fake, 256, 128, fake, 256, ctypes.byref(opts),
-                        None) == 1                                                    # no tiled
+                        None) == 1                                                    # no variant 3
     opts = w4.GemmOpts(1, 9)
     assert L.w4a16_gemm(fake, 512, 4, 512, fake, 256, 128, fake, 256, ctypes.byref(opts),
                         None) == 1                                                    # > 8 waves

@@ -260,12 +260,19 @@ def _decode_layers():
 @pytest.mark.parametrize("cfg_idx,shape_idx,key,ms", _decode_layers())
 def test_linear_full_size_decode(cfg_idx, shape_idx, key, ms):
     """The decode workload's layers at full size, M = 1, 4, 16 as the bench
-    runs them: A8/s_a bit-exact with the oracle, and Y and acc identical to
-    the two-launch path on every output."""
+    runs them: A8/s_a bit-exact with the oracle, acc bit-exact and Y within
+    tolerance of the oracle on 64 sampled columns (plus the first and last
+    and both ends of a middle 16-column tile), and Y and acc identical to the
+    two-launch path on every output."""
     layer, n, k, g, dist = key
     w = synth.weights(n, k, seed=synth.weight_seed(cfg_idx, shape_idx, 0), dist=dist)
     blob = w4.pack(w, g)
+    rng = np.random.default_rng(500 + shape_idx)
+    mid = (n // 32) * 16
+    cols = np.unique(np.concatenate([[0, n - 1, mid, mid + 15], rng.choice(n, 64, replace=False)]))
+    qw = ref.quantize_weights(w[cols], g)
     del w
+    w8hat = ref.decoded_weights(qw)
     for mi, m in enumerate(ms):
         a = synth.activations(m, k, seed=synth.act_seed(cfg_idx, shape_idx, mi))
         log(f"linear full-size {layer} m={m} n={n} k={k}")
@@ -273,6 +280,9 @@ def test_linear_full_size_decode(cfg_idx, shape_idx, key, ms):
         want_a8, want_sa = ref.quant_act(a)
         assert np.array_equal(s_a.view(np.uint16), want_sa.view(np.uint16))
         assert np.array_equal(a8, want_a8)
+        acc_ref = ref.gemm_acc(want_a8, w8hat)
+        assert np.array_equal(acc[:, cols], acc_ref)
+        assert ref.y_tolerance_ok(y[:, cols], ref.epilogue(acc_ref, want_sa, qw["s1"])).all()
         y2, acc2 = _run_two_launch(a, blob, n, k, g)
         assert np.array_equal(acc, acc2)
         assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))

@@ -32,6 +32,8 @@ def _run(a_np, blob, n, k, g, **kw):
     (33, 112, 256, 0, "student_t4"),
     (64, 512, 1152, 128, "normal"),
     (5, 4112, 2688, 64, "student_t4"),
+    (100, 512, 1024, 128, "normal"),          # skinny above 64 tokens: the tiled grid would be 4 tiles
+    (128, 272, 640, 64, "student_t4"),
 ])
 def test_w4a16_matches_oracle(m, n, k, g, dist):
     w = synth.weights(n, k, seed=800 + n + k, dist=dist)
@@ -100,3 +102,48 @@ def test_w4a16_vs_w4a8_same_weights():
     y16_ref = y16_ref.astype(np.float64)
     rel_ref = np.linalg.norm(out["y"].astype(np.float64) - y16_ref) / np.linalg.norm(y16_ref)
     assert abs(rel_gpu - rel_ref) < 1e-3 * max(1.0, rel_ref * 100), (rel_gpu, rel_ref)
+
+
+@pytest.mark.parametrize("m,n,k,g,dist,variant", [
+    (65, 144, 384, 64, "normal", 0),          # ragged rows and a workgroup with one real column tile
+    (300, 256, 1024, 128, "student_t4", 0),   # two row tiles, the second ragged
+    (257, 400, 640, 32, "normal", 0),
+    (128, 128, 256, 0, "student_t4", 0),      # per-channel
+    (1, 48, 384, 128, "normal", 2),           # the tiled kernel forced at one token
+    (40, 272, 768, 64, "normal", 2),
+    (512, 1024, 2048, 128, "student_t4", 0),
+])
+def test_w4a16_tiled_matches_oracle(m, n, k, g, dist, variant):
+    """The tiled W4A16 kernel (M > 64, or forced): every output within the
+    fp32 summation bound of the oracle's exact sum."""
+    w = synth.weights(n, k, seed=810 + n + k, dist=dist)
+    a = synth.activations(m, k, seed=910 + m)
+    qw = ref.quantize_weights(w, g)
+    y_ref, _, sum_abs = ref.w4a16_linear(a, qw)
+    log(f"w4a16 tiled m={m} n={n} k={k} g={g} variant={variant}")
+    y = _run(a, w4.pack(w, g), n, k, g, variant=variant)
+    ok = ref.y16_tolerance_ok(y, y_ref, sum_abs, k)
+    assert ok.all(), np.argwhere(~ok)[:5]
+
+
+def test_w4a16_tiled_full_size_sampled():
+    """The batched Llama-3-8B QKV and down layers at M = 256 and 1024 on the
+    tiled kernel: 64 sampled output columns (plus the first and last), all
+    rows, against the oracle."""
+    import torch
+    dev = device()
+    for (n, k) in ((6144, 4096), (4096, 14336)):
+        w = synth.weights(n, k, seed=n + k + 1)
+        blob = w4.to_device(w4.pack(w, 128), dev)
+        rng = np.random.default_rng(n + 1)
+        cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 64, replace=False)]))
+        qw = ref.quantize_weights(w[cols], 128)
+        del w
+        for m in (256, 1024):
+            a = synth.activations(m, k, seed=m + k + 1)
+            log(f"w4a16 tiled full-size m={m} n={n} k={k}")
+            y = w4.w4a16(torch.from_numpy(a).to(dev), blob, n, k, 128)
+            torch.cuda.synchronize()
+            y_s = y.cpu().numpy()[:, cols]
+            y_ref, _, sum_abs = ref.w4a16_linear(a, qw)
+            assert ref.y16_tolerance_ok(y_s, y_ref, sum_abs, k).all()

@@ -481,20 +481,18 @@ extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
   if (!a_dev || !blob_dev || !y_dev) return W4A8_ERR_INVALID_ARGUMENT;
   if (lda < k || lda % 8 || ldy < n) return W4A8_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
-  if (opts && (opts->variant > 1 || opts->variant < 0 || !opts_in_range(opts)))
+  if (opts && (opts->variant > 2 || opts->variant < 0 || !opts_in_range(opts)))
     return W4A8_ERR_INVALID_ARGUMENT;
-  if (m > 64 || g == W4A8_CODEBOOK_NF) return W4A8_ERR_UNSUPPORTED;
-  // one row tile per workgroup (more row tiles go to grid.y): fp16 operands
-  // take twice the registers of int8 ones, and a deeper row tile would spill
-  SkinnyConfig c = choose_skinny(std::min(m, 16), n, k);
-  c.mr = 1;
-  if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
-  if (opts && opts->k_split > 0) {
-    c.kw = opts->k_split;
-    c.kbw = blocks_per_wave(k / kKBlock, c.kw);
-  }
+  if (g == W4A8_CODEBOOK_NF) return W4A8_ERR_UNSUPPORTED;
+  // automatic choice: the skinny kernel (one 16-row tile per workgroup, the
+  // weights streamed once per row tile) up to 64 tokens, and up to 128 when
+  // the tiled kernel's grid would hold fewer than 128 workgroups of 256 x 128
+  // (it has no K split, so such a grid leaves most compute units idle)
+  const long w16_tiles = ((long(m) + 255) / 256) * ((long(n) / 16 + 7) / 8);
+  const int variant = opts && opts->variant ? opts->variant
+                                            : (m <= 64 || (m <= 128 && w16_tiles < 128) ? 1 : 2);
+  if (variant == 1 && m > 128) return W4A8_ERR_UNSUPPORTED;
   const int gpb = groups_per_block(k, g);
-  if (!skinny_config_supported(c, k, gpb)) return W4A8_ERR_INVALID_ARGUMENT;
   Sections sec = sections(n, k, g);
   const uint8_t* base = static_cast<const uint8_t*>(blob_dev);
   Gemm16Params p{};
@@ -509,6 +507,20 @@ extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
   p.meta_row_bytes = sec.meta_row_bytes;
   p.y = y_dev;
   p.ldy = ldy;
+  if (variant == 2) {
+    if (w16_tiles > kMaxWorkgroups) return W4A8_ERR_UNSUPPORTED;
+    return device_status(launch_w4a16_tiled(p, gpb, static_cast<hipStream_t>(stream)));
+  }
+  // one row tile per workgroup (more row tiles go to grid.y): fp16 operands
+  // take twice the registers of int8 ones, and a deeper row tile would spill
+  SkinnyConfig c = choose_skinny(std::min(m, 16), n, k);
+  c.mr = 1;
+  if (opts && opts->n_tiles > 0) c.nc = opts->n_tiles;
+  if (opts && opts->k_split > 0) {
+    c.kw = opts->k_split;
+    c.kbw = blocks_per_wave(k / kKBlock, c.kw);
+  }
+  if (!skinny_config_supported(c, k, gpb)) return W4A8_ERR_INVALID_ARGUMENT;
   return device_status(launch_w4a16_skinny(p, gpb, c, static_cast<hipStream_t>(stream)));
 }
 

@@ -97,6 +97,8 @@ bool skinny_config_supported(const SkinnyConfig& c, int k, int gpb);
 
 hipError_t launch_w4a16_skinny(const Gemm16Params& p, int gpb, const SkinnyConfig& c,
                                hipStream_t stream);
+// W4A16 tiled kernel (w4a16.hip): 256 x 128 tiles for larger M, any m >= 1.
+hipError_t launch_w4a16_tiled(const Gemm16Params& p, int gpb, hipStream_t stream);
 
 // Fused quantization + skinny GEMM (fused.hip): M <= kFusedMaxRows, one
 // row tile, 1 or 2 column tiles per group, 4, 8 or 16 k-blocks per wave with

@@ -23,6 +23,7 @@
 
 #include "gemm_common.h"
 #include "kernels.h"
+#include "tile_common.h"
 
 namespace w4a8 {
 namespace {
@@ -218,6 +219,157 @@ __global__ __launch_bounds__(512) void w4a16_skinny_kernel(Gemm16Params p) {
   }
 }
 
+// ------------------------------------------------------------------ tiled
+// Larger M: the fp16 MFMA becomes the bound, as in the W4A8 tiled kernel.
+// A workgroup of 2 x 4 waves computes a 256 x 128 tile; wave (rg, cg) owns
+// the 8 row tiles of row group rg and the 2 column tiles of column group cg.
+// Each 128-k block's fp16 activation tile (256 rows x 256 bytes), weight
+// codes and group meta go from HBM to LDS with direct-to-LDS buffer loads,
+// two stages deep, one barrier per k-block.  The activation tile's 16-byte
+// chunks are XOR-swizzled by row (16 chunks per row) so that the 16 rows a
+// ds_read_b128 of a quarter-wave covers fall on distinct banks.
+constexpr int kW16Rows = 256, kW16Cols = 128;
+
+template <int GPB>
+__global__ __launch_bounds__(512, 1) void w4a16_tiled_kernel(Gemm16Params p) {
+  using namespace tile;
+  constexpr int MR = 8, NC = 2, NW = 4, S = 2;
+  constexpr int A_BYTES = kW16Rows * 256;            // 128 k of fp16 per row
+  constexpr int W_BYTES = NW * NC * 1024;
+  constexpr int M_BYTES = NW * NC * 256;
+  constexpr int STAGE = A_BYTES + W_BYTES + M_BYTES;
+  constexpr int CPW = A_BYTES / (16 * 512);          // activation chunks per lane
+  constexpr int LOADS = CPW + 2;
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cg = wave % NW;
+  const int rg = wave / NW;
+  const int quarter = lane >> 4;
+  const int r16 = lane & 15;
+
+  const int ntiles = p.n >> 4;
+  const int kblocks = p.k >> 7;
+  const int nbm = (p.m + kW16Rows - 1) / kW16Rows;
+  const int nbn = (ntiles + NW * NC - 1) / (NW * NC);
+  int bm, bn;
+  tile_of(blockIdx.x, nbm, nbn, &bm, &bn);
+  const int row0 = bm * kW16Rows;
+  const int wtile0 = bn * NW * NC;                   // first column tile of the workgroup
+  const int tile0 = wtile0 + cg * NC;                // first column tile of this wave
+
+  // each wave loads the codes and meta of one of the workgroup's 8 tiles
+  const int my_tile = min(wtile0 + wave, ntiles - 1);
+  const __amdgpu_buffer_rsrc_t q_rsrc =
+      make_rsrc(p.q + size_t(my_tile) * kblocks * 1024, uint32_t(kblocks) * 1024u);
+  const __amdgpu_buffer_rsrc_t m_rsrc =
+      make_rsrc(p.meta + size_t(my_tile) * 16 * p.meta_row_bytes, 16u * uint32_t(p.meta_row_bytes));
+  const uint32_t q_lane = uint32_t(lane) * 16;
+  const uint32_t m_lane = uint32_t(r16) * uint32_t(p.meta_row_bytes);
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      make_rsrc(p.a + size_t(row0) * p.lda, uint32_t(kW16Rows) * uint32_t(p.lda) * 2u);
+  uint32_t a_lane[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int s = (wave * CPW + j) * 64 + lane;      // 16-byte slot of the LDS tile
+    const int row = s >> 4;
+    const int chunk = (s & 15) ^ (row & 15);
+    a_lane[j] = (uint32_t(min(row0 + row, p.m - 1) - row0) * uint32_t(p.lda) + uint32_t(chunk * 8)) * 2u;
+  }
+
+  v4f acc[MR][NC];
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  v2h s1s1[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint16_t s1 = p.s1[min((tile0 + c) * 16 + r16, p.n - 1)];
+    s1s1[c] = __builtin_bit_cast(v2h, uint32_t(s1) | (uint32_t(s1) << 16));
+  }
+
+  auto issue = [&](int kb, int stage) {
+    uint8_t* st = smem + stage * STAGE;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+      buffer_to_lds16(a_rsrc, st + (wave * CPW + j) * 1024, a_lane[j], uint32_t(kb) * 256u);
+    buffer_to_lds16(q_rsrc, st + A_BYTES + wave * 1024, q_lane, uint32_t(kb) * 1024u);
+    buffer_to_lds4(m_rsrc, st + A_BYTES + W_BYTES + wave * 256, m_lane,
+                   GPB == 0 ? 0u : uint32_t((kb * GPB) >> 2) * 4u);
+  };
+  auto compute = [&](int kb, const uint8_t* st) {
+    u32x4 qv[NC];
+    uint32_t mv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qv[c] = *reinterpret_cast<const u32x4*>(st + A_BYTES + (cg * NC + c) * 1024 + lane * 16);
+      mv[c] = *reinterpret_cast<const uint32_t*>(st + A_BYTES + W_BYTES + (cg * NC + c) * 256 + lane * 4);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int byte = 0;
+      if (GPB == 1) byte = kb & 3;
+      if (GPB == 2) byte = 2 * (kb & 1) + h;
+      if (GPB == 4) byte = 2 * h + (quarter >> 1);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        v8h af[MR];
+        const int chunk = (8 * h + 2 * quarter + s) ^ r16;   // rows rg*128 + 16i + r16
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+          af[i] = *reinterpret_cast<const v8h*>(st + (rg * 128 + i * 16 + r16) * 256 + chunk * 16);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint32_t w = s ? (h ? qv[c].w : qv[c].y) : (h ? qv[c].z : qv[c].x);
+          const v8h bf = decode8_f16(w, group_const((mv[c] >> (8 * byte)) & 0xFFu), s1s1[c]);
+#pragma unroll
+          for (int i = 0; i < MR; ++i)
+            acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, acc[i][c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // stage k % 2 holds k-block k; the loads of k-block k + 1 go to the other
+  // stage after the barrier that follows every wave's last read of it
+  issue(0, 0);
+  for (int k = 0; k < kblocks; ++k) {
+    wait_vm<0>();                  // this wave's loads of k-block k have landed
+    __builtin_amdgcn_s_barrier();
+    if (k + 1 < kblocks) issue(k + 1, (k + 1) & 1);
+    compute(k, smem + (k & 1) * STAGE);
+  }
+
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = (tile0 + c) * 16 + r16;
+      if (tile0 + c >= ntiles) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + rg * 128 + i * 16 + 4 * quarter + r;
+        if (row < p.m) p.y[size_t(row) * p.ldy + col] = f2h_bits(acc[i][c][r]);
+      }
+    }
+}
+
+template <int GPB>
+hipError_t launch_w4a16_tiled_t(const Gemm16Params& p, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&w4a16_tiled_kernel<GPB>);
+  const size_t lds = size_t(2) * (kW16Rows * 256 + 4 * 2 * (1024 + 256));
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  const int nbm = (p.m + kW16Rows - 1) / kW16Rows;
+  const int nbn = (p.n / 16 + kW16Cols / 16 - 1) / (kW16Cols / 16);
+  Gemm16Params arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(fn, dim3(nbm * nbn), dim3(512), args, lds, stream);
+}
+
 template <int MR, int NC, int GPB>
 hipError_t launch_w4a16_t(const Gemm16Params& p, const SkinnyConfig& c, hipStream_t stream) {
   constexpr int D = 4;
@@ -244,6 +396,16 @@ hipError_t w4a16_by_gpb(const Gemm16Params& p, int gpb, const SkinnyConfig& c, h
 }
 
 }  // namespace
+
+hipError_t launch_w4a16_tiled(const Gemm16Params& p, int gpb, hipStream_t stream) {
+  switch (gpb) {
+    case 0: return launch_w4a16_tiled_t<0>(p, stream);
+    case 1: return launch_w4a16_tiled_t<1>(p, stream);
+    case 2: return launch_w4a16_tiled_t<2>(p, stream);
+    case 4: return launch_w4a16_tiled_t<4>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_w4a16_skinny(const Gemm16Params& p, int gpb, const SkinnyConfig& c,
                                hipStream_t stream) {
