@@ -319,7 +319,7 @@ __global__ __launch_bounds__(512) void fused_kernel(GemmParams p, const uint16_t
         if constexpr (GPB < 0) {
           bf = decode16_lut(w0, w1);
         } else {
-          bf = decode16(w0, w1, group_const((ms[c] >> (8 * byte)) & 0xFFu));
+          bf = decode16(w0, w1, group_const_at(ms[c], 8u * byte));
         }
         acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[c], 0, 0, 0);
       }

@@ -55,15 +55,20 @@ struct GroupConst {
   uint32_t cccc;  // (128 - z*s2) in all four bytes
 };
 
-__device__ __forceinline__ GroupConst group_const(uint32_t mb) {
+// The constants of the group whose meta byte starts at bit `sh` of the
+// dword m (low nibble z, high nibble s2 - 1): two bit-field extracts, two
+// 24-bit multiply-adds (s2 = (s2 - 1) + 1 folded into both), a subtract
+// and a byte splat.
+__device__ __forceinline__ GroupConst group_const_at(uint32_t m, uint32_t sh) {
+  const uint32_t s2m1 = __builtin_amdgcn_ubfe(m, sh + 4u, 4u);
+  const uint32_t z = __builtin_amdgcn_ubfe(m, sh, 4u);
   GroupConst g;
-  uint32_t s2 = (mb >> 4) + 1u;
-  uint32_t z = mb & 15u;
-  g.s2s2 = s2 | (s2 << 16);
-  uint32_t c = 128u - __umul24(z, s2);
-  g.cccc = __builtin_amdgcn_perm(0u, c, 0u);  // replicate byte 0
+  g.s2s2 = __umul24(s2m1, 0x10001u) + 0x10001u;            // s2 | s2 << 16
+  const uint32_t zs2 = __umul24(z, s2m1) + z;               // z * s2
+  g.cccc = __builtin_amdgcn_perm(0u, 128u - zs2, 0u);       // replicate byte 0
   return g;
 }
+
 
 __device__ __forceinline__ uint32_t dec4(uint32_t nibbles, GroupConst g) {
   return pk_mad_u16(nibbles, g.s2s2, g.cccc) ^ 0x80808080u;

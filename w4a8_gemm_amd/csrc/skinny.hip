@@ -151,7 +151,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(GemmParams p) {
         if constexpr (GPB < 0) {
           bf[c] = decode16_lut(w0, w1);
         } else {
-          const GroupConst gc = group_const((ms[c] >> (8 * byte)) & 0xFFu);
+          const GroupConst gc = group_const_at(ms[c], 8u * byte);
           bf[c] = decode16(w0, w1, gc);
         }
       }

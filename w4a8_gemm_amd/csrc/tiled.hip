@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * kColGroups * RW * KG, 2 / (RW * KG)) void tile
     if (GPB >= 0 && GPB <= 1) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        gblk[c] = group_const((mv[c] >> (GPB == 1 ? 8 * (kb & 3) : 0)) & 0xFFu);
+        gblk[c] = group_const_at(mv[c], GPB == 1 ? 8u * (kb & 3) : 0u);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(64 * kColGroups * RW * KG, 2 / (RW * KG)) void tile
           bf[c] = decode16_lut(w0, w1);
         } else {
           const GroupConst gc =
-              GPB <= 1 ? gblk[c] : group_const((mv[c] >> (8 * byte)) & 0xFFu);
+              GPB <= 1 ? gblk[c] : group_const_at(mv[c], 8u * byte);
           bf[c] = decode16(w0, w1, gc);
         }
       }
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(512, 1) void tiled_pp_kernel(GemmParams p) {
     if (GPB >= 0 && GPB <= 1) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        gblk[c] = group_const((mv[c] >> (GPB == 1 ? 8 * (kb & 3) : 0)) & 0xFFu);
+        gblk[c] = group_const_at(mv[c], GPB == 1 ? 8u * (kb & 3) : 0u);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(512, 1) void tiled_pp_kernel(GemmParams p) {
           bf[h][c] = decode16_lut(w0, w1);
         } else {
           const GroupConst gc =
-              GPB <= 1 ? gblk[c] : group_const((mv[c] >> (8 * byte)) & 0xFFu);
+              GPB <= 1 ? gblk[c] : group_const_at(mv[c], 8u * byte);
           bf[h][c] = decode16(w0, w1, gc);
         }
       }

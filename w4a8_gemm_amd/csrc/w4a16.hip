@@ -141,7 +141,7 @@ __global__ __launch_bounds__(512) void w4a16_skinny_kernel(Gemm16Params p) {
       if (GPB == 4) byte = 2 * h + (quarter >> 1);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const GroupConst gc = group_const((ms[c] >> (8 * byte)) & 0xFFu);
+        const GroupConst gc = group_const_at(ms[c], 8u * byte);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const uint32_t w = s ? (h ? qs[c].w : qs[c].y) : (h ? qs[c].z : qs[c].x);
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(512, 1) void w4a16_tiled_kernel(Gemm16Params p) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const uint32_t w = s ? (h ? qv[c].w : qv[c].y) : (h ? qv[c].z : qv[c].x);
-          const v8h bf = decode8_f16(w, group_const((mv[c] >> (8 * byte)) & 0xFFu), s1s1[c]);
+          const v8h bf = decode8_f16(w, group_const_at(mv[c], 8u * byte), s1s1[c]);
 #pragma unroll
           for (int i = 0; i < MR; ++i)
             acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, acc[i][c], 0, 0, 0);
