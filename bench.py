@@ -191,39 +191,55 @@ def cpu_baseline(runs, weights, acts, unit, budget_s=15.0, rows_max=CPU_ROWS, co
     except Exception:
         cores = os.cpu_count() or 1
     qws = {key: ref.quantize_weights(w[:cols_max], key[2]) for key, w in weights.items()}
-    done_bytes = done_ops = 0.0
-    stage = {"quant_act": 0.0, "decode_and_gemm": 0.0, "epilogue": 0.0}
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        for (m, layer, n, k, g, seed, key) in runs:
-            a = acts[(m, key)][:rows_max]
-            qw = qws[key]
-            t1 = time.perf_counter()
-            a8, s_a = ref.quant_act(a)
-            t2 = time.perf_counter()
-            acc = ref.gemm_acc(a8, ref.decoded_weights(qw))
-            t3 = time.perf_counter()
-            ref.epilogue(acc, s_a, qw["s1"])
-            t4 = time.perf_counter()
-            stage["quant_act"] += t2 - t1
-            stage["decode_and_gemm"] += t3 - t2
-            stage["epilogue"] += t4 - t3
-            rows, cols = a.shape[0], min(cols_max, n)
-            done_bytes += algo_bytes(rows, cols, k, g) + quant_bytes(rows, k)
-            done_ops += 2.0 * rows * cols * k
-        passes += 1
-        if time.perf_counter() - t0 >= budget_s or passes >= 500:
-            break
-    dt = time.perf_counter() - t0
-    value = done_ops / dt / 1e12 if unit == "TOPS" else done_bytes / dt / 1e9
+
+    def timed(budget):
+        done_bytes = done_ops = 0.0
+        stage = {"quant_act": 0.0, "decode_and_gemm": 0.0, "epilogue": 0.0}
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            for (m, layer, n, k, g, seed, key) in runs:
+                a = acts[(m, key)][:rows_max]
+                qw = qws[key]
+                t1 = time.perf_counter()
+                a8, s_a = ref.quant_act(a)
+                t2 = time.perf_counter()
+                acc = ref.gemm_acc(a8, ref.decoded_weights(qw))
+                t3 = time.perf_counter()
+                ref.epilogue(acc, s_a, qw["s1"])
+                t4 = time.perf_counter()
+                stage["quant_act"] += t2 - t1
+                stage["decode_and_gemm"] += t3 - t2
+                stage["epilogue"] += t4 - t3
+                rows, cols = a.shape[0], min(cols_max, n)
+                done_bytes += algo_bytes(rows, cols, k, g) + quant_bytes(rows, k)
+                done_ops += 2.0 * rows * cols * k
+            passes += 1
+            if time.perf_counter() - t0 >= budget or passes >= 500:
+                break
+        dt = time.perf_counter() - t0
+        value = done_ops / dt / 1e12 if unit == "TOPS" else done_bytes / dt / 1e9
+        return value, passes, dt, stage
+
+    value, passes, dt, stage = timed(budget_s)
+    # the same sample with the BLAS pool held to one thread
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            v1, p1, d1, _ = timed(budget_s / 3)
+        single = {"value": round(v1, 6), "unit": unit, "cores": 1,
+                  "sample": f"the same sample, {p1} pass(es), {d1:.1f} s"}
+    except Exception as e:   # threadpoolctl missing or unable to limit
+        single = {"value": None, "reason": str(e)[:120]}
     return {"value": round(value, 6), "unit": unit, "cores": int(cores),
             "kind": "oracle",
             "sample": f"every run of the workload restricted to its first {rows_max} tokens and "
                       f"first {cols_max} output columns (all of K), {passes} pass(es), "
                       f"{dt:.1f} s",
             "cpu_model": cpu_model(), "nproc": os.cpu_count(),
-            "stage_seconds": {key: round(v, 3) for key, v in stage.items()}}
+            "stage_seconds": {key: round(v, 3) for key, v in stage.items()},
+            "single_thread": single}
 
 
 # ------------------------------------------------------------------ stream probe
