@@ -85,6 +85,12 @@ typedef enum {
 #define W4A8_N_MAX (1 << 22)
 #define W4A8_ACT_K_MAX (1 << 30)
 
+/* Upper bound on the row strides of the activations the GEMM entry points
+ * read (lda8 of the int8 A8, lda of the fp16 A), in elements.  The tiled
+ * kernels address a 256-row activation tile through one buffer descriptor
+ * with a 32-bit range; larger strides are rejected with INVALID_ARGUMENT. */
+#define W4A8_LD_MAX (1 << 22)
+
 const char* w4a8_status_string(w4a8_status s);
 
 /* Text of the HIP error behind the most recent W4A8_ERR_DEVICE returned to
@@ -175,8 +181,8 @@ w4a8_status w4a8_quant_act_static(const uint16_t* a_dev, int m, int k, int lda,
  * moving weights from global memory dominates); large M is bound by the
  * int8 matrix cores, the regime of the kernel speedups the LiquidGEMM page
  * reports ("Результаты").
- *   a8_dev    m x k int8, row stride lda8 bytes (lda8 >= k, lda8 % 16 == 0,
- *             16-byte aligned)
+ *   a8_dev    m x k int8, row stride lda8 bytes (k <= lda8 <= W4A8_LD_MAX,
+ *             lda8 % 16 == 0, 16-byte aligned)
  *   s_a_dev   m fp16 per-token scales
  *   blob_dev  device copy of a w4a8_pack blob for (n, k, g)
  *   y_dev     m x n fp16 output, row stride ldy elements (ldy >= n)
@@ -269,10 +275,10 @@ w4a8_status w4a8_gemm_noalloc(const int8_t* a8_dev, int lda8, const uint16_t* s_
  * most 16 blocks; opts->workgroups sets its grid.)
  * Outputs are bit-identical either way (Y to the last bit: the same int32
  * sums, scales and epilogue).
- *   a_dev     m x k fp16, row stride lda elements (lda >= k, lda % 8 == 0,
- *             16-byte aligned)
- *   a8_dev, s_a_dev   outputs, as w4a8_quant_act (lda8 >= k, lda8 % 16 == 0,
- *             16-byte aligned)
+ *   a_dev     m x k fp16, row stride lda elements (k <= lda <= W4A8_LD_MAX,
+ *             lda % 8 == 0, 16-byte aligned)
+ *   a8_dev, s_a_dev   outputs, as w4a8_quant_act (k <= lda8 <= W4A8_LD_MAX,
+ *             lda8 % 16 == 0, 16-byte aligned)
  *   other arguments as w4a8_gemm; opts->variant may also be 3 to force the
  *   fused kernel (UNSUPPORTED where it does not apply); the workspace is the
  *   one w4a8_gemm_workspace_size gives for the same arguments.
@@ -291,8 +297,9 @@ w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
  * (one rounding), summed in fp32 on the fp16 MFMA:
  *   Y[m,n] = fp16(sum_k A[m,k] * W16^[n,k])
  * There is no activation quantization and no s_a.
- *   a_dev   m x k fp16, row stride lda elements (lda >= k, lda % 8 == 0,
- *           16-byte aligned); y_dev m x n fp16, row stride ldy >= n.
+ *   a_dev   m x k fp16, row stride lda elements (k <= lda <= W4A8_LD_MAX,
+ *           lda % 8 == 0, 16-byte aligned); y_dev m x n fp16, row stride
+ *           ldy >= n.
  *   opts    NULL for the automatic choice (the skinny kernel up to 64
  *           tokens, and up to 128 where the tiled grid would hold fewer than
  *           128 tiles; the tiled one above); variant 1 forces the skinny

@@ -406,6 +406,26 @@ def test_w4a16_validates_before_any_hip_call():
 
 
 
+def test_row_strides_are_bounded():
+    """Activation row strides above W4A8_LD_MAX are refused before any HIP
+    call (the tiled kernels address 256 rows through one 32-bit buffer range)."""
+    L = w4.lib
+    fake = ctypes.c_void_p(4096)
+    big = (1 << 22) + 16
+    ws = ctypes.c_void_p(8192)
+    # w4a8_gemm(a8, lda8, s_a, m, blob, n, k, g, y, ldy, acc, ldacc, ws, ws_bytes, opts, stream)
+    assert L.w4a8_gemm(fake, big, fake, 4, fake, 256, 512, 128, fake, 256, None, 0, ws, 1 << 20,
+                       None, None) == 1
+    assert L.w4a8_gemm_noalloc(fake, big, fake, 4, fake, 256, 512, 128, fake, 256, None, 0,
+                               None, None) == 1
+    # w4a8_linear(a, lda, m, k, blob, n, g, y, ldy, a8, lda8, s_a, acc, ldacc, ws, ws_bytes, opts, stream)
+    assert L.w4a8_linear(fake, big, 4, 512, fake, 256, 128, fake, 256, fake, 512, fake, None, 0,
+                         ws, 1 << 20, None, None) == 1
+    assert L.w4a8_linear(fake, 512, 4, 512, fake, 256, 128, fake, 256, fake, big, fake, None, 0,
+                         ws, 1 << 20, None, None) == 1
+    assert L.w4a16_gemm(fake, big, 4, 512, fake, 256, 128, fake, 256, None, None) == 1
+
+
 def test_read_probe_validates_before_any_hip_call():
     L = w4.lib
     fake = ctypes.c_void_p(4096)

@@ -271,7 +271,7 @@ bool gemm_args_ok(const int8_t* a8_dev, int lda8, const uint16_t* s_a_dev, const
                   int n, int k, const uint16_t* y_dev, int ldy, const int32_t* acc_dev,
                   int ldacc) {
   if (!a8_dev || !s_a_dev || !blob_dev || !y_dev) return false;
-  if (lda8 < k || lda8 % 16 || ldy < n || (acc_dev && ldacc < n)) return false;
+  if (lda8 < k || lda8 % 16 || lda8 > W4A8_LD_MAX || ldy < n || (acc_dev && ldacc < n)) return false;
   return aligned16(a8_dev) && aligned16(blob_dev);
 }
 
@@ -427,7 +427,8 @@ extern "C" w4a8_status w4a8_linear(const uint16_t* a_dev, int lda, int m, int k,
   if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   if (m == 0) return W4A8_OK;
   if (!a_dev || !blob_dev || !y_dev || !a8_dev || !s_a_dev) return W4A8_ERR_INVALID_ARGUMENT;
-  if (lda < k || lda % 8 || lda8 < k || lda8 % 16 || ldy < n || (acc_dev && ldacc < n))
+  if (lda < k || lda % 8 || lda > W4A8_LD_MAX || lda8 < k || lda8 % 16 || lda8 > W4A8_LD_MAX ||
+      ldy < n || (acc_dev && ldacc < n))
     return W4A8_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_dev) || !aligned16(a8_dev) || !aligned16(blob_dev))
     return W4A8_ERR_INVALID_ARGUMENT;
@@ -479,7 +480,7 @@ extern "C" w4a8_status w4a16_gemm(const uint16_t* a_dev, int lda, int m, int k,
   if (!gemm_shape_supported(n, k, g)) return W4A8_ERR_UNSUPPORTED;
   if (m == 0) return W4A8_OK;
   if (!a_dev || !blob_dev || !y_dev) return W4A8_ERR_INVALID_ARGUMENT;
-  if (lda < k || lda % 8 || ldy < n) return W4A8_ERR_INVALID_ARGUMENT;
+  if (lda < k || lda % 8 || lda > W4A8_LD_MAX || ldy < n) return W4A8_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_dev) || !aligned16(blob_dev)) return W4A8_ERR_INVALID_ARGUMENT;
   if (opts && (opts->variant > 2 || opts->variant < 0 || !opts_in_range(opts)))
     return W4A8_ERR_INVALID_ARGUMENT;
