@@ -247,6 +247,15 @@ def test_gemm_tiled_k_slices_exact(m, n, k, g):
         torch.cuda.synchronize()
         assert np.array_equal(acc.cpu().numpy(), out["acc"]), (sl, mt, nt, st, ks)
         assert ref.y_tolerance_ok(y.cpu().numpy(), out["y"]).all()
+    # the 256 x 256 ping-pong kernel with its K split over workgroups
+    for sl in (2, 3, min(kblocks, 5)):
+        ws = torch.full((16 * m * n * 4 + 64,), 0x5A, dtype=torch.uint8, device=dev)
+        log(f"gemm ping-pong slices={sl} m={m} n={n} k={k} g={g}")
+        y, acc = w4.gemm(a8, s_a, wdev, n, k, g, want_acc=True, variant=2, row_groups=2,
+                         slices=sl, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), out["acc"]), ("ping-pong", sl)
+        assert ref.y_tolerance_ok(y.cpu().numpy(), out["y"]).all()
 
 
 def test_gemm_extreme_operands():

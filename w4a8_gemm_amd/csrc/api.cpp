@@ -165,6 +165,13 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   //   M <= 64 (or <= 128 with K <= 16384), K >= 8192, < 192 tiles of 64 x 128
   //                                      -> 64 x 128 with K split over 2..16
   //                                         workgroups (~256 in all)
+  //   M >= 1024, K >= 12288, < 224 of 256 x 256
+  //                                      -> 256 x 256 (ping-pong) with K split
+  //                                         so that ~256 workgroups run, each
+  //                                         slice >= 16 k-blocks (the 1024 x
+  //                                         4096 x 14336 down projection: 81
+  //                                         against 90 us for 128 x 256 split
+  //                                         three ways)
   //   K >= 8192 and < 192 of 128 x 256   -> 128 x 256 with K split over
   //                                         2..8 workgroups (~384 in all)
   //   >= 256 tiles of 128 x 128, M > 64 -> 128 x 128, four waves, 3 stages
@@ -204,6 +211,9 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     c = TiledConfig{4, 2, 4, 1, 1, 3};
     const long want = 256 / tiled_tiles(m, n, 64, 128);
     slices = int(std::max(2L, std::min<long>(want, kMaxSlices)));
+  } else if (m >= 1024 && kblocks >= 96 && t256 >= 32) {
+    c = TiledConfig{8, 4, 4, 2, 1, 3};
+    slices = int(std::max(2L, std::min<long>({256 / t256, 8L, long(kblocks / 16)})));
   } else if (kblocks >= 64 && t128x256 < 192) {
     c = TiledConfig{8, 4, 4, 1, 1, 2};
     const long want = (384 + t128x256 - 1) / t128x256;
