@@ -127,19 +127,19 @@ def test_w4a16_tiled_matches_oracle(m, n, k, g, dist, variant):
 
 
 def test_w4a16_tiled_full_size_sampled():
-    """The batched Llama-3-8B QKV and down layers at M = 256 and 1024 on the
-    tiled kernel: 64 sampled output columns (plus the first and last), all
-    rows, against the oracle."""
+    """The batched Llama-3-8B QKV and down layers at M = 256 and 1024 and the
+    Qwen1.5-72B O layer at M = 2048 on the tiled kernel: 64 sampled output
+    columns (plus the first and last), all rows, against the oracle."""
     import torch
     dev = device()
-    for (n, k) in ((6144, 4096), (4096, 14336)):
+    for (n, k) in ((6144, 4096), (4096, 14336), (8192, 8192)):
         w = synth.weights(n, k, seed=n + k + 1)
         blob = w4.to_device(w4.pack(w, 128), dev)
         rng = np.random.default_rng(n + 1)
         cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 64, replace=False)]))
         qw = ref.quantize_weights(w[cols], 128)
         del w
-        for m in (256, 1024):
+        for m in ((256, 1024) if k != 8192 else (2048,)):
             a = synth.activations(m, k, seed=m + k + 1)
             log(f"w4a16 tiled full-size m={m} n={n} k={k}")
             y = w4.w4a16(torch.from_numpy(a).to(dev), blob, n, k, 128)

@@ -87,3 +87,21 @@ def test_noalloc_forced_split():
     with pytest.raises(w4.W4A8Error) as err:
         w4.gemm_noalloc(a8b, s_ab, blob, n, k, g, yb, slices=2)   # 2 x 64 MiB of partials
     assert err.value.status == 3
+
+
+def test_noalloc_ping_pong_split_fills_the_scratch():
+    """The Llama-3-8B down projection at M = 1024 splits K four ways on the
+    256 x 256 ping-pong kernel: 1024 x 4096 x 4 slices of int32 partials fill
+    the 64 MiB scratch exactly.  The allocation-free call keeps that split and
+    equals w4a8_gemm; the accumulators equal the oracle's on sampled columns."""
+    m, n, k, g = 1024, 4096, 14336, 128
+    assert w4.lib.w4a8_gemm_workspace_size(m, n, k, g, None) == 64 << 20
+    w, blob, a8, s_a, a8_np, s_a_np = _inputs(m, n, k, g, 23)
+    log(f"gemm_noalloc ping-pong split m={m} n={n} k={k}")
+    y, acc, y_ref, acc_ref = _both(m, n, k, g, blob, a8, s_a)
+    assert np.array_equal(acc, acc_ref)
+    assert np.array_equal(y.view(np.uint16), y_ref.view(np.uint16))
+    cols = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(23).choice(n, 32)]))
+    qw = ref.quantize_weights(w[cols], g)
+    want = ref.gemm_acc(a8_np, ref.decoded_weights(qw))
+    assert np.array_equal(acc[:, cols], want)
