@@ -168,10 +168,5 @@ __device__ __forceinline__ v4i decode16_lut(uint32_t w0, uint32_t w1) {
   return b;
 }
 
-// Meta byte of group `grp` for a lane whose row pointer is mrow.
-__device__ __forceinline__ uint32_t meta_byte(const uint8_t* mrow, int grp) {
-  return mrow[grp];
-}
-
 }  // namespace dev
 }  // namespace w4a8
