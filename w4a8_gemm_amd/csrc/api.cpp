@@ -174,10 +174,14 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   //                                         three ways)
   //   K >= 8192 and < 192 of 128 x 256   -> 128 x 256 with K split over
   //                                         2..8 workgroups (~384 in all)
-  //   >= 256 tiles of 128 x 128, M > 64 -> 128 x 128, four waves, 3 stages
-  //   >= 192 tiles of 128 x 128, M > 64 -> 128 x 128, two k-groups, 2 stages
+  //   > 256 tiles of 128 x 128, M > 64  -> 128 x 128, four waves, 3 stages
+  //   > 256 tiles of 64 x 128, M > 64   -> 128 x 128, two k-groups, 2 stages
   //   otherwise                          -> 64 x 128, two k-groups, 3 stages
-  // (at M <= 64 a 128-row tile is half empty: 64 x 128 tiles, same count)
+  // (the eight-wave kernels run one workgroup per compute unit, so each
+  // keeps its tiles to one round of 256 workgroups: 512 x 5120 x 5120 takes
+  // 34 us on 160 tiles of 128 x 128 against 41 on 320 of 64 x 128, and the
+  // 1024 x 4096 x 4096 layer 29 against 31 us with four waves per tile;
+  // at M <= 64 a 128-row tile is half empty: 64 x 128 tiles, same count)
   // Forced options select among the four-wave kernels (or the eight-wave
   // ones they name) with the rest from the 128 x 256 defaults.
   TiledConfig& c = pl.tiled;
@@ -218,9 +222,9 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     c = TiledConfig{8, 4, 4, 1, 1, 2};
     const long want = (384 + t128x256 - 1) / t128x256;
     slices = int(std::max(2L, std::min<long>(want, 8)));
-  } else if (m > 64 && t128x128 >= 256) {
+  } else if (m > 64 && t128x128 > 256) {
     c = TiledConfig{8, 2, 4, 1, 1, 3};
-  } else if (m > 64 && t128x128 >= 192) {
+  } else if (m > 64 && tiled_tiles(m, n, 64, 128) > 256) {
     c = TiledConfig{8, 2, 4, 1, 2, 2};
   } else {
     c = TiledConfig{4, 2, 4, 1, 2, 3};
