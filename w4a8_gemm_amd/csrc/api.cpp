@@ -161,11 +161,12 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   // shapes, M = 32 .. 1024): the kernel needs about one workgroup of eight
   // waves, or two of four, per compute unit, so the tile shrinks with the
   // grid it yields:
-  //   >= 224 tiles of 256 x 256          -> 256 x 256, eight waves, 3 stages
+  //   >= 192 tiles of 256 x 256 whose rounds beat 128 x 128 ones (below)
+  //                                      -> 256 x 256, eight waves, 3 stages
   //   M <= 64 (or <= 128 with K <= 16384), K >= 8192, < 192 tiles of 64 x 128
   //                                      -> 64 x 128 with K split over 2..16
   //                                         workgroups (~256 in all)
-  //   M >= 1024, K >= 12288, < 224 of 256 x 256
+  //   M >= 1024, K >= 12288, < 384 of 128 x 128 (and not the above)
   //                                      -> 256 x 256 (ping-pong) with K split
   //                                         so that ~256 workgroups run, each
   //                                         slice >= 16 k-blocks (the 1024 x
@@ -191,6 +192,14 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   const long t128x128 = tiled_tiles(m, n, 128, 128);
   const bool forced = opts && (opts->m_tiles > 0 || opts->stages > 0 || opts->k_split > 0 ||
                                opts->row_groups > 0 || opts->n_tiles > 0 || opts->slices > 0);
+  // 256 x 256 tiles run one workgroup per compute unit, 128 x 128 four-wave
+  // tiles two: whole rounds of 256 and 512 workgroups, a round of 128 x 128
+  // tiles costing about 0.6 of a 256 x 256 one (sweeps at K = 4096-8192:
+  // 0.58-0.65).  So the ping-pong kernel is taken when its rounds win, which
+  // keeps a 258- or 324-tile grid off a nearly empty second round
+  // (1536 x 11008 x 4096: 105 against 124 us).
+  const bool pp_rounds_win =
+      t256 >= 192 && 5 * ((t256 + 255) / 256) < 3 * ((t128x128 + 511) / 512);
   int slices = 1;
   if (forced) {
     c.nc = 4;
@@ -204,7 +213,7 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     if (opts->stages > 0) c.stages = opts->stages;
     if (opts->n_tiles > 0) c.nc = opts->n_tiles;
 
-  } else if (t256 >= 224) {
+  } else if (pp_rounds_win) {
     c = TiledConfig{8, 4, 4, 2, 1, 3};
   } else if ((m <= 64 || (m <= 128 && kblocks <= 128)) && kblocks >= 64 &&
              tiled_tiles(m, n, 64, 128) < 192) {
@@ -215,7 +224,7 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     c = TiledConfig{4, 2, 4, 1, 1, 3};
     const long want = 256 / tiled_tiles(m, n, 64, 128);
     slices = int(std::max(2L, std::min<long>(want, kMaxSlices)));
-  } else if (m >= 1024 && kblocks >= 96 && t256 >= 32) {
+  } else if (m >= 1024 && kblocks >= 96 && t256 >= 32 && t128x128 < 384) {
     c = TiledConfig{8, 4, 4, 2, 1, 3};
     slices = int(std::max(2L, std::min<long>({256 / t256, 8L, long(kblocks / 16)})));
   } else if (kblocks >= 64 && t128x256 < 192) {
