@@ -143,9 +143,17 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   // (its activation fragments, re-read by every workgroup, grow with M), or
   // K is long enough that those re-reads (M * K bytes per workgroup) cost
   // more than splitting K over workgroups
-  const bool split_small = m > 16 && m <= 64 && kblocks >= 64 && long(m) * k >= kSplitSmallElems;
+  const long t64 = tiled_tiles(m, n, 64, 128);
+  // ... or, from 40 tokens and K >= 4096, the layer has 80-191 such tiles
+  // (over ~10k columns): there 64 x 128 tiles with K split in two beat the
+  // skinny kernel by 15-37 % at K = 4096-5120 (11008, 13824 and 16384
+  // columns), while up to 64 tiles the skinny kernel stays ahead at every
+  // M <= 48
+  const bool split_small = m > 16 && m <= 64 &&
+                           ((kblocks >= 64 && long(m) * k >= kSplitSmallElems) ||
+                            (m >= 40 && kblocks >= 32 && t64 >= 80 && t64 < 192));
   if (pl.variant == 0)
-    pl.variant = (m <= 16 || (m <= 64 && tiled_tiles(m, n, 64, 128) < 192 && !split_small)) ? 1 : 2;
+    pl.variant = (m <= 16 || (m <= 64 && t64 < 192 && !split_small)) ? 1 : 2;
   if (pl.variant == 1) {
     if (m > 64) { pl.status = W4A8_ERR_UNSUPPORTED; return pl; }
     SkinnyConfig& c = pl.skinny;
@@ -217,12 +225,13 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
 
   } else if (pp_rounds_win) {
     c = TiledConfig{8, 4, 4, 2, 1, 3};
-  } else if ((m <= 64 || (m <= 128 && kblocks <= 128)) && kblocks >= 64 &&
+  } else if ((split_small || ((m <= 64 || (m <= 128 && kblocks <= 128)) && kblocks >= 64)) &&
              tiled_tiles(m, n, 64, 128) < 192) {
-    // 17..128 tokens, long K (up to 16384 above 64 tokens): 64 x 128 tiles,
-    // K split so that ~256 workgroups run (each slice re-reads only its part
-    // of A8); at 96-128 tokens 20-25 % faster than 128 x 256 tiles on the
-    // 4096 x 14336 and 8192 x 8192 layers, slower at K = 24576
+    // 17..128 tokens, long K (up to 16384 above 64 tokens), or 40..64 tokens
+    // on wide layers: 64 x 128 tiles, K split so that ~256 workgroups run
+    // (each slice re-reads only its part of A8); at 96-128 tokens 20-25 %
+    // faster than 128 x 256 tiles on the 4096 x 14336 and 8192 x 8192
+    // layers, slower at K = 24576
     c = TiledConfig{4, 2, 4, 1, 1, 3};
     const long want = 256 / tiled_tiles(m, n, 64, 128);
     slices = int(std::max(2L, std::min<long>(want, kMaxSlices)));
