@@ -275,6 +275,28 @@ def test_gemm_workspace_size():
     opts = w4.GemmOpts(2, 0, 0, 0, 0, 0, 17)                 # beyond 16 slices: invalid, none
     assert L.w4a8_gemm_workspace_size(100, 256, 4096, 128, ctypes.byref(opts)) == 0
     assert L.w4a8_gemm_workspace_size(256, 4096, 14336, 96, None) == 0     # unsupported g
+
+
+def test_plan_splits_follow_the_measured_regimes():
+    """The automatic plan's K splits, read through the workspace size (one
+    int32 plane of M x N per slice): the skinny kernel (no split) up to 32
+    tokens on wide layers and up to 64 tiles of 64 x 128 at any M <= 64;
+    64 x 128 tiles split in two from 40 tokens on 80-191 such tiles; at
+    129-192 tokens 64 x 128 tiles split towards ~384 workgroups; none on
+    grids that fill the GPU."""
+    L = w4.lib
+    plane = lambda m, n: m * n * 4
+    assert L.w4a8_gemm_workspace_size(32, 11008, 4096, 128, None) == 0        # skinny
+    assert L.w4a8_gemm_workspace_size(64, 6144, 4096, 128, None) == 0         # skinny (48 tiles)
+    assert L.w4a8_gemm_workspace_size(48, 11008, 4096, 128, None) == 2 * plane(48, 11008)
+    assert L.w4a8_gemm_workspace_size(64, 16384, 4096, 128, None) == 2 * plane(64, 16384)
+    assert L.w4a8_gemm_workspace_size(48, 11008, 2048, 128, None) == 0        # K < 4096: skinny
+    # 160 tokens, 96 tiles of 64 x 128: ceil(384 / 96) = 4 slices
+    assert L.w4a8_gemm_workspace_size(160, 4096, 11008, 128, None) == 4 * plane(160, 4096)
+    # 192 tokens, 120 tiles: ceil(384 / 120) = 4, at most K / 2048 = 6
+    assert L.w4a8_gemm_workspace_size(192, 5120, 13824, 128, None) == 4 * plane(192, 5120)
+    assert L.w4a8_gemm_workspace_size(1536, 11008, 4096, 128, None) == 0      # full grid
+    assert L.w4a8_gemm_workspace_size(1536, 8192, 8192, 128, None) == 0
     assert L.w4a8_gemm_workspace_size(0, 4096, 14336, 128, None) == 0
 
 
