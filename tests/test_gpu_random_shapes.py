@@ -20,13 +20,19 @@ import w4a8_gemm_amd as w4
 from gpu_util import device, log
 from oracle import ref
 
-# (name, smallest M, largest M, largest K / 128)
+# (name, smallest M, largest M, K / 128 range, 16-column tiles range)
 REGIMES = [
-    ("decode", 1, 16, 112),
-    ("small", 17, 64, 112),
-    ("mid", 65, 700, 64),
-    ("large", 701, 2304, 64),
-    ("long_k", 1024, 1536, 128),
+    ("decode", 1, 16, (1, 112), (1, 1023)),
+    ("small", 17, 64, (1, 112), (1, 1023)),
+    ("mid", 65, 700, (1, 64), (1, 1023)),
+    ("large", 701, 2304, (1, 64), (1, 1023)),
+    ("long_k", 1024, 1536, (96, 128), (1, 1023)),
+    # 40-64 tokens, K >= 4096, 80-191 tiles of 64 x 128: split 64 x 128 tiles
+    ("wide_small", 40, 64, (32, 36), (640, 1528)),
+    # 129-192 tokens, 8192 <= K <= 16384, < 192 tiles of 64 x 128
+    ("m129_192", 129, 192, (64, 128), (64, 504)),
+    # 200-700 tokens, K >= 8192, few 128 x 256 tiles: 128 x 256 split
+    ("split_mid", 200, 700, (64, 112), (64, 400)),
 ]
 MAX_WEIGHTS = 48 * 2 ** 20      # N * K drawn at most (host memory for the fp32 weights)
 MAX_ACTS = 24 * 2 ** 20         # M * K
@@ -34,11 +40,10 @@ MAX_ACTS = 24 * 2 ** 20         # M * K
 
 def draw(seed):
     rng = np.random.default_rng(7919 * seed + 13)
-    name, m_lo, m_hi, kb_hi = REGIMES[seed % len(REGIMES)]
+    name, m_lo, m_hi, (kb_lo, kb_hi), (t_lo, t_hi) = REGIMES[seed % len(REGIMES)]
     m = int(rng.integers(m_lo, m_hi + 1))
-    kb_lo = 96 if name == "long_k" else 1
     k = 128 * int(rng.integers(kb_lo, kb_hi + 1))
-    n = 16 * int(rng.integers(1, 1024))
+    n = 16 * int(rng.integers(t_lo, t_hi + 1))
     n = max(16, min(n, MAX_WEIGHTS // k // 16 * 16))
     if name == "long_k":
         # 32-223 tiles of 256 x 256 (the ping-pong kernel with K split)
@@ -50,7 +55,7 @@ def draw(seed):
     return name, m, n, k, g, dist
 
 
-CASES = [draw(s) for s in range(30)]
+CASES = [draw(s) for s in range(40)]
 
 
 @pytest.mark.gpu
@@ -85,11 +90,21 @@ def test_linear_random_shape(seed):
 
 def test_draws_cover_every_regime():
     """The draws reach each plan regime, including the split ping-pong one
-    (M >= 1024, K >= 12288, 32-223 tiles of 256 x 256)."""
+    (M >= 1024, K >= 12288, 32-223 tiles of 256 x 256), and the K-split
+    regimes take the split the plan is meant to choose (read through the
+    workspace size: one int32 plane of M x N per slice)."""
     names = {c[0] for c in CASES}
     assert names == {r[0] for r in REGIMES}
     assert {c[4] for c in CASES} == {32, 64, 128, 0}
-    long_k = [c for c in CASES if c[0] == "long_k"]
-    for _, m, n, k, _, _ in long_k:
-        tiles = ((m + 255) // 256) * ((n // 16 + 15) // 16)
-        assert k >= 12288 and 32 <= tiles < 224
+    for name, m, n, k, g, _ in CASES:
+        t64 = ((m + 63) // 64) * ((n // 16 + 7) // 8)
+        slices = w4.lib.w4a8_gemm_workspace_size(m, n, k, g, None) // (m * n * 4)
+        if name == "long_k":
+            tiles = ((m + 255) // 256) * ((n // 16 + 15) // 16)
+            assert k >= 12288 and 32 <= tiles < 224
+        if name == "wide_small":
+            assert 80 <= t64 < 192 and slices == max(2, 256 // t64)
+        if name == "m129_192":
+            assert t64 < 192 and slices >= 2
+        if name == "split_mid":
+            assert slices >= 2
