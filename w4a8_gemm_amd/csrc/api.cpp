@@ -226,23 +226,21 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
   } else if (pp_rounds_win) {
     c = TiledConfig{8, 4, 4, 2, 1, 3};
   } else if ((split_small || ((m <= 64 || (m <= 128 && kblocks <= 128)) && kblocks >= 64)) &&
-             tiled_tiles(m, n, 64, 128) < 192) {
+             t64 < 192) {
     // 17..128 tokens, long K (up to 16384 above 64 tokens), or 40..64 tokens
     // on wide layers: 64 x 128 tiles, K split so that ~256 workgroups run
     // (each slice re-reads only its part of A8); at 96-128 tokens 20-25 %
     // faster than 128 x 256 tiles on the 4096 x 14336 and 8192 x 8192
     // layers, slower at K = 24576
     c = TiledConfig{4, 2, 4, 1, 1, 3};
-    const long want = 256 / tiled_tiles(m, n, 64, 128);
-    slices = int(std::max(2L, std::min<long>(want, kMaxSlices)));
-  } else if (m > 128 && m <= 192 && kblocks >= 64 && kblocks <= 128 &&
-             tiled_tiles(m, n, 64, 128) < 192) {
+    slices = int(std::max(2L, std::min<long>(256 / t64, kMaxSlices)));
+  } else if (m > 128 && m <= 192 && kblocks >= 64 && kblocks <= 128 && t64 < 192) {
     // 129..192 tokens: three 64-row tiles waste less than two 128-row ones,
-    // and with K split so that ~384 workgroups run (two per compute unit fit)
-    // 17-19 % faster than 128 x 256 tiles split over 8 (M = 160 and 192 on
-    // 4096 x 11008 and 5120 x 13824; equal on 4096 x 14336)
+    // and with K split so that ~384 workgroups run (two per compute unit
+    // fit) 11-50 % faster than 128 x 256 tiles split over 8 (M = 129, 160
+    // and 192 on 4096 x 11008, 5120 x 13824 and 2048 x 8192; within 2 % on
+    // 4096 x 14336)
     c = TiledConfig{4, 2, 4, 1, 1, 3};
-    const long t64 = tiled_tiles(m, n, 64, 128);
     slices = int(std::max(2L, std::min<long>((384 + t64 - 1) / t64, kblocks / 16)));
   } else if (m >= 1024 && kblocks >= 96 && t256 >= 32 && t128x128 < 384) {
     c = TiledConfig{8, 4, 4, 2, 1, 3};
@@ -253,7 +251,7 @@ Plan plan_gemm(int m, int n, int k, const w4a8_gemm_opts* opts) {
     slices = int(std::max(2L, std::min<long>(want, 8)));
   } else if (m > 64 && t128x128 > 256) {
     c = TiledConfig{8, 2, 4, 1, 1, 3};
-  } else if (m > 64 && tiled_tiles(m, n, 64, 128) > 256) {
+  } else if (m > 64 && t64 > 256) {
     c = TiledConfig{8, 2, 4, 1, 2, 2};
   } else {
     c = TiledConfig{4, 2, 4, 1, 2, 3};
