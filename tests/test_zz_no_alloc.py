@@ -105,3 +105,22 @@ def test_noalloc_ping_pong_split_fills_the_scratch():
     qw = ref.quantize_weights(w[cols], g)
     want = ref.gemm_acc(a8_np, ref.decoded_weights(qw))
     assert np.array_equal(acc[:, cols], want)
+
+
+@pytest.mark.parametrize("m,n,k", [(48, 11008, 4096), (160, 4096, 11008)])
+def test_noalloc_split_regimes_of_the_plan(m, n, k):
+    """The K-split plans at 40-64 tokens on wide layers (two slices) and at
+    129-192 tokens (towards ~384 workgroups) through the static scratch: the
+    same split as w4a8_gemm's workspace, identical results, and accumulators
+    equal to the oracle's on sampled columns."""
+    g = 128
+    need = w4.lib.w4a8_gemm_workspace_size(m, n, k, g, None)
+    assert 0 < need <= 64 * 2 ** 20, "the plan must split K within the scratch"
+    w, blob, a8, s_a, a8_np, s_a_np = _inputs(m, n, k, g, m + n)
+    log(f"gemm_noalloc split regime m={m} n={n} k={k}")
+    y, acc, y_ref, acc_ref = _both(m, n, k, g, blob, a8, s_a)
+    assert np.array_equal(acc, acc_ref)
+    assert np.array_equal(y.view(np.uint16), y_ref.view(np.uint16))
+    cols = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(m).choice(n, 32)]))
+    qw = ref.quantize_weights(w[cols], g)
+    assert np.array_equal(acc[:, cols], ref.gemm_acc(a8_np, ref.decoded_weights(qw)))
