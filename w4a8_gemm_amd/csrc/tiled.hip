@@ -539,8 +539,11 @@ hipError_t pp_by_gpb(const GemmParams& p, int gpb, int sl, hipStream_t s) {
 
 // Sum of the K slices' int32 partial tiles (exact) and the epilogue
 // Y = fp16((acc * s_a) * s1).  One thread per 4 consecutive outputs, so the
-// partial rows are read with coalesced 16-byte loads.
-__global__ __launch_bounds__(256) void split_reduce_kernel(GemmParams p, int slices) {
+// partial rows are read with coalesced 16-byte loads, the 4 column scales
+// with one 8-byte load (the s1 section is 256-byte aligned and col % 4 == 0)
+// and, when Y's rows allow it, the 4 outputs are written with one 8-byte
+// store.
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmParams p, int slices, int y_vec) {
   const int n4 = p.n >> 2;
   const long idx = long(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= long(p.m) * n4) return;
@@ -551,11 +554,23 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmParams p, int sli
   v4i t = src[0];
   for (int sl = 1; sl < slices; ++sl) t += src[sl * (plane >> 2)];
   const float sa = h2f(p.s_a[row]);
+  const uint2 s1x4 = *reinterpret_cast<const uint2*>(p.s1 + col);
+  const uint16_t s1v[4] = {uint16_t(s1x4.x), uint16_t(s1x4.x >> 16), uint16_t(s1x4.y),
+                           uint16_t(s1x4.y >> 16)};
+  uint16_t yv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float y = (static_cast<float>(t[j]) * sa) * h2f(p.s1[col + j]);
-    p.y[size_t(row) * p.ldy + col + j] = f2h_bits(y);
-    if (p.acc) p.acc[size_t(row) * p.ldacc + col + j] = t[j];
+  for (int j = 0; j < 4; ++j) yv[j] = f2h_bits((static_cast<float>(t[j]) * sa) * h2f(s1v[j]));
+  uint16_t* dst = p.y + size_t(row) * p.ldy + col;
+  if (y_vec) {
+    *reinterpret_cast<uint2*>(dst) =
+        uint2{uint32_t(yv[0]) | (uint32_t(yv[1]) << 16), uint32_t(yv[2]) | (uint32_t(yv[3]) << 16)};
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = yv[j];
+  }
+  if (p.acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p.acc[size_t(row) * p.ldacc + col + j] = t[j];
   }
 }
 
@@ -647,7 +662,8 @@ hipError_t launch_split_reduce(const GemmParams& p, int slices, hipStream_t stre
   const long threads = long(p.m) * (p.n / 4);
   GemmParams arg = p;
   int sl = slices;
-  void* args[] = {&arg, &sl};
+  int y_vec = (reinterpret_cast<uintptr_t>(p.y) % 8 == 0) && (p.ldy % 4 == 0);
+  void* args[] = {&arg, &sl, &y_vec};
   return hipLaunchKernel(reinterpret_cast<const void*>(&split_reduce_kernel),
                          dim3(unsigned((threads + 255) / 256)), dim3(256), args, 0, stream);
 }
